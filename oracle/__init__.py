@@ -1,0 +1,175 @@
+"""CPU oracle for the fused attention forward — TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The product library never does, and the oracle shares no
+code with it: ``oracle.c`` is plain C compiled by gcc, this module is argument
+marshalling through ctypes.
+
+Functions (each wraps the C function of the same name; see ``oracle.c`` for
+the definitions and the passages they follow):
+
+* :func:`attn` — exact attention in fp64 over all rows or a row sample.
+* :func:`quant_int8`, :func:`quant_e4m3` — per-64-token-block codes + scales.
+* :func:`e4m3_encode`, :func:`e4m3_decode` — the OCP E4M3 format.
+* :func:`attn_quant` — quantised-mode emulation (diagnostic).
+
+Pins: every function is checked in ``tests/test_oracle_*.py`` against closed
+forms, invariants, brute force and library special cases. ``attn_quant`` is
+pinned only through closed-form special cases (uniform scores; exactly
+representable inputs) — its general output has no independent reference.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", "-pthread", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        i, i64, d = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        vp = ctypes.c_void_p
+        lib.oracle_attn.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d,
+                                    vp, i64, vp, vp, vp, i]
+        lib.oracle_attn.restype = i
+        lib.oracle_attn_quant.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+                                          d, vp, i64, vp, i]
+        lib.oracle_attn_quant.restype = i
+        lib.oracle_quant_int8.argtypes = [vp, i, i64, i, i, vp, vp]
+        lib.oracle_quant_int8.restype = i
+        lib.oracle_quant_e4m3.argtypes = [vp, i, i64, i, i, vp, vp]
+        lib.oracle_quant_e4m3.restype = i
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_float
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _cpu(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype not in DTYPE_CODE:
+        raise TypeError("oracle inputs must be float32, float16 or bfloat16")
+    return t.detach().to("cpu").contiguous()
+
+
+def attn(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None,
+         want_lse=False, want_weights=False, nthreads=None):
+    """Exact fp64 attention. q: [B,Hq,Nq,D]; k, v: [B,Hkv,Nk,D] (same dtype).
+
+    ``rows``: optional int64 flat indices (b*Hq + h)*Nq + i. Returns out
+    [nrows, D] (or [B,Hq,Nq,D] when rows is None) as float64 numpy, plus lse
+    and weights if asked.
+    """
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if rows is None:
+        nrows = B * Hq * Nq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    lse = np.zeros(nrows, dtype=np.float64) if want_lse else None
+    w = np.zeros((nrows, Nk), dtype=np.float64) if want_weights else None
+    rc = _load().oracle_attn(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), float(scale),
+        None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        out.ctypes.data, None if lse is None else lse.ctypes.data,
+        None if w is None else w.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn rejected the arguments")
+    if rows is None:
+        out = out.reshape(B, Hq, Nq, D)
+    res = [out]
+    if want_lse:
+        res.append(lse)
+    if want_weights:
+        res.append(w)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def attn_quant(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None,
+               nthreads=None):
+    """Quantised-mode emulation (see oracle.c). Same conventions as attn()."""
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if rows is None:
+        nrows, rows_arr = B * Hq * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_attn_quant(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), float(scale),
+        None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        out.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_quant failed")
+    return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+def _quant(fn, x, code_dtype):
+    x = _cpu(x)
+    *lead, N, D = x.shape
+    BH = int(np.prod(lead)) if lead else 1
+    nblk = (N + 63) // 64
+    codes = np.zeros(x.shape, dtype=code_dtype)
+    scales = np.zeros(tuple(lead) + (nblk,), dtype=np.float32)
+    rc = fn(x.data_ptr(), DTYPE_CODE[x.dtype], BH, N, D, codes.ctypes.data,
+            scales.ctypes.data)
+    if rc != 0:
+        raise ValueError("quantiser rejected the arguments")
+    return codes, scales
+
+
+def quant_int8(x):
+    """INT8 codes [..., N, D] (int8) and scales [..., ceil(N/64)] (float32)."""
+    return _quant(_load().oracle_quant_int8, x, np.int8)
+
+
+def quant_e4m3(x):
+    """E4M3 codes [..., N, D] (uint8) and scales [..., ceil(N/64)] (float32)."""
+    return _quant(_load().oracle_quant_e4m3, x, np.uint8)
+
+
+def e4m3_encode(y: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(y)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(code)))

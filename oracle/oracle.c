@@ -1,0 +1,458 @@
+/*
+ * oracle.c — plain, slow, obviously-correct CPU reference for the fused
+ * attention forward and its low-precision preparation.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or
+ * calls this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do. It shares no code, header, table or constant with the
+ * HIP path.
+ *
+ * What it computes (each function cites the passage it follows):
+ *
+ *   oracle_attn         exact attention, O = softmax(scale * Q K^T + mask) V,
+ *                       in double precision, one query row at a time, with the
+ *                       score row materialised (no tiling, no online softmax).
+ *                       The pages name this operation ("attention" of shape
+ *                       1 x 40 heads x 32 760 tokens x 128 in the table of
+ *                       section 1 of "Attention kernels on a home RTX 5080")
+ *                       but never write its formula; the textbook definition
+ *                       of scaled-dot-product attention is used.
+ *   oracle_quant_int8   symmetric per-block INT8 codes for Q and K ("INT8 QK",
+ *                       same table), one fp32 scale per 64-token block of one
+ *                       head.
+ *   oracle_quant_e4m3   per-block FP8 E4M3 codes for V ("FP8 PV", same table).
+ *   oracle_e4m3_encode  / oracle_e4m3_decode: the OCP FP8 E4M3 ("E4M3FN")
+ *                       format, written from its definition (sign, 4 exponent
+ *                       bits biased by 7, 3 mantissa bits, subnormals, no
+ *                       infinities, 0x7F/0xFF NaN).
+ *   oracle_attn_quant   the quantised-mode emulation: exact attention on the
+ *                       dequantised Q, K, V with every softmax weight passed
+ *                       through E4M3 at the static scale 448 (a diagnostic).
+ *
+ * Readings taken where the pages are silent (listed again in the design
+ * notes): query row i sits at absolute position pos0 + i and key j at j; a
+ * key is visible iff j >= window_lo and (not causal or j <= pos0 + i); the KV
+ * head of query head h is h / (Hq / Hkv); a row with no visible key is all
+ * zeros ("zeroed inactive regions", section "measured results" of "round 21
+ * track b — qsa2"); quantisation blocks are 64 consecutive tokens of one
+ * head, the last block holding the remainder.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ *        -pthread oracle.c -o liboracle.so -lm
+ * (no contraction: the fp32 quantiser arithmetic must round after every op).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Element types of the raw inputs. */
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+/* ---------------------------------------------------------------- inputs -- */
+
+/* IEEE binary16 -> double, from the format definition (exact). */
+static double half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int m = h & 1023;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24);
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25);
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16 -> double: the upper half of an IEEE binary32 (exact). */
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+  switch (dtype) {
+    case OR_F32: return (double)((const float*)base)[idx];
+    case OR_F16: return half_to_double(((const uint16_t*)base)[idx]);
+    default:     return bf16_to_double(((const uint16_t*)base)[idx]);
+  }
+}
+
+/* Same, but to float (exact for all three types). */
+static float load_elem_f(const void* base, int dtype, int64_t idx) {
+  return (float)load_elem(base, dtype, idx);
+}
+
+/* ------------------------------------------------------ exact attention -- */
+
+typedef struct {
+  const void *q, *k, *v;
+  int dtype;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal, window_lo, pos0;
+  double scale;
+  const int64_t* rows;   /* NULL: all rows in order */
+  int64_t nrows;
+  double* out;           /* nrows x D */
+  double* lse;           /* nrows, may be NULL */
+  double* weights;       /* nrows x Nk, may be NULL */
+  /* quantised-mode emulation (NULL for exact attention) */
+  const double* qhat;    /* dequantised inputs, same layouts as q/k/v */
+  const double* khat;
+  const double* vhat;
+  int quant_p;           /* 1: pass each weight through E4M3 at scale 448 */
+  int64_t next;          /* work counter */
+  pthread_mutex_t mu;
+} attn_job;
+
+uint8_t oracle_e4m3_encode(float y);
+float oracle_e4m3_decode(uint8_t code);
+
+/* Key j is visible to query row i. */
+static int visible(const attn_job* J, int i, int j) {
+  if (j < J->window_lo) return 0;
+  if (J->causal && j > J->pos0 + i) return 0;
+  return j < J->Nk;
+}
+
+static double q_at(const attn_job* J, int64_t idx) {
+  return J->qhat ? J->qhat[idx] : load_elem(J->q, J->dtype, idx);
+}
+static double k_at(const attn_job* J, int64_t idx) {
+  return J->khat ? J->khat[idx] : load_elem(J->k, J->dtype, idx);
+}
+static double v_at(const attn_job* J, int64_t idx) {
+  return J->vhat ? J->vhat[idx] : load_elem(J->v, J->dtype, idx);
+}
+
+/* One query row, by the definition: scores, max, exp, sum, weighted sum. */
+static void attn_one_row(const attn_job* J, int64_t slot, double* s) {
+  int64_t r = J->rows ? J->rows[slot] : slot;
+  int i = (int)(r % J->Nq);
+  int64_t bh = r / J->Nq;
+  int h = (int)(bh % J->Hq);
+  int b = (int)(bh / J->Hq);
+  int g = h / (J->Hq / J->Hkv);
+  int D = J->D, Nk = J->Nk;
+  int64_t qoff = r * D;
+  int64_t kvoff = ((int64_t)b * J->Hkv + g) * Nk * D;
+  double* o = J->out + slot * D;
+
+  double m = -INFINITY;
+  int any = 0;
+  for (int j = 0; j < Nk; ++j) {
+    if (!visible(J, i, j)) continue;
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d)
+      acc += q_at(J, qoff + d) * k_at(J, kvoff + (int64_t)j * D + d);
+    s[j] = J->scale * acc;
+    if (s[j] > m) m = s[j];
+    any = 1;
+  }
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (J->weights)
+    for (int j = 0; j < Nk; ++j) J->weights[slot * Nk + j] = 0.0;
+  if (!any) {
+    if (J->lse) J->lse[slot] = -INFINITY;
+    return;
+  }
+  double l = 0.0;
+  for (int j = 0; j < Nk; ++j) {
+    if (!visible(J, i, j)) continue;
+    double p = exp(s[j] - m);
+    l += p;
+    double pv = p;
+    if (J->quant_p) {
+      float scaled = (float)(448.0 * p);
+      pv = (double)oracle_e4m3_decode(oracle_e4m3_encode(scaled)) / 448.0;
+    }
+    for (int d = 0; d < D; ++d) o[d] += pv * v_at(J, kvoff + (int64_t)j * D + d);
+    s[j] = p;
+  }
+  for (int d = 0; d < D; ++d) o[d] /= l;
+  if (J->lse) J->lse[slot] = m + log(l);
+  if (J->weights)
+    for (int j = 0; j < Nk; ++j)
+      if (visible(J, i, j)) J->weights[slot * Nk + j] = s[j] / l;
+}
+
+static void* attn_worker(void* arg) {
+  attn_job* J = (attn_job*)arg;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
+  if (!s) return (void*)1;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t slot = J->next;
+    J->next += 16;
+    pthread_mutex_unlock(&J->mu);
+    if (slot >= J->nrows) break;
+    int64_t end = slot + 16 < J->nrows ? slot + 16 : J->nrows;
+    for (; slot < end; ++slot) attn_one_row(J, slot, s);
+  }
+  free(s);
+  return NULL;
+}
+
+static int run_attn(attn_job* J, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  J->next = 0;
+  pthread_mutex_init(&J->mu, NULL);
+  int started = 0, rc = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, attn_worker, J) != 0) break;
+    ++started;
+  }
+  if (attn_worker(J) != NULL) rc = -1;
+  for (int t = 1; t <= started; ++t) {
+    void* res = NULL;
+    pthread_join(th[t], &res);
+    if (res != NULL) rc = -1;
+  }
+  pthread_mutex_destroy(&J->mu);
+  return rc;
+}
+
+static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
+  if (Hq % Hkv != 0) return -1;
+  return 0;
+}
+
+/*
+ * Exact attention in double precision.
+ *   q: [B][Hq][Nq][D], k and v: [B][Hkv][Nk][D], all of element type dtype,
+ *   row-major with D innermost (the "1 x 40 heads x 32 760 tokens x 128"
+ *   order of the table in section 1 of "Attention kernels on a home RTX
+ *   5080").
+ *   rows: flat row indices r = (b*Hq + h)*Nq + i to evaluate, or NULL for all
+ *   B*Hq*Nq rows in order; out receives nrows x D doubles.
+ *   lse (nullable): m + ln(l) per row, -inf for a row with no visible key.
+ *   weights (nullable): nrows x Nk softmax weights, 0 where masked.
+ * Returns 0, or -1 on a bad shape.
+ */
+int oracle_attn(const void* q, const void* k, const void* v, int dtype,
+                int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                int causal, int window_lo, int pos0, double scale,
+                const int64_t* rows, int64_t nrows,
+                double* out, double* lse, double* weights, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  attn_job J;
+  memset(&J, 0, sizeof J);
+  J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+  J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+  J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale;
+  J.rows = rows;
+  J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+  J.out = out; J.lse = lse; J.weights = weights;
+  return run_attn(&J, nthreads);
+}
+
+/* ------------------------------------------------------------ FP8 E4M3 -- */
+
+/*
+ * Decode an OCP FP8 E4M3 code: sign bit, exponent field e (bias 7), mantissa
+ * field m. e = 0 holds the subnormals m * 2^-9; e = 15 with m = 7 is NaN (the
+ * format has no infinities, so e = 15, m < 7 are ordinary values up to 448).
+ */
+float oracle_e4m3_decode(uint8_t code) {
+  int sign = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  float v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexpf((float)m, -9);
+  else        v = ldexpf((float)(8 + m), e - 10);
+  return sign ? -v : v;
+}
+
+/*
+ * Encode to E4M3 by brute force: the nearest of the 127 non-negative finite
+ * magnitudes (codes 0x00..0x7E), ties to the code with an even mantissa field
+ * (round-to-nearest-even); sign carried separately. Inputs beyond 448 in
+ * magnitude saturate to 448 (callers clamp first; the quantiser never sees
+ * them). NaN input gives 0x7F.
+ */
+uint8_t oracle_e4m3_encode(float y) {
+  if (isnan(y)) return 0x7F;
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double err = fabs((double)oracle_e4m3_decode((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* ---------------------------------------------------------- quantisers -- */
+
+/*
+ * Per-block symmetric INT8 codes ("INT8 QK" in the table of section 1 of
+ * "Attention kernels on a home RTX 5080"; one scale per block of 64 tokens of
+ * one head).
+ *   x: [BH][N][D] of element type dtype; codes: same layout, int8;
+ *   scales: [BH][ceil(N/64)] fp32.
+ * Per block, in fp32 with round-to-nearest-even after every operation:
+ *   amax = max |x|;  amax == 0 -> scale 0, all codes 0;
+ *   otherwise scale = amax / 127, inv = 127 / amax,
+ *             code = clamp(rint(x * inv), -127, 127).
+ * Dequantisation is code * scale.
+ */
+int oracle_quant_int8(const void* x, int dtype, int64_t BH, int N, int D,
+                      int8_t* codes, float* scales) {
+  if (BH < 1 || N < 1 || D < 1) return -1;
+  int nblk = (N + 63) / 64;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    for (int t = 0; t < nblk; ++t) {
+      int r0 = 64 * t, r1 = r0 + 64 < N ? r0 + 64 : N;
+      int64_t base = (bh * N + r0) * (int64_t)D;
+      int64_t cnt = (int64_t)(r1 - r0) * D;
+      float amax = 0.0f;
+      for (int64_t e = 0; e < cnt; ++e) {
+        float a = fabsf(load_elem_f(x, dtype, base + e));
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) {
+        scales[bh * nblk + t] = 0.0f;
+        for (int64_t e = 0; e < cnt; ++e) codes[base + e] = 0;
+        continue;
+      }
+      volatile float s = amax / 127.0f;
+      volatile float inv = 127.0f / amax;
+      scales[bh * nblk + t] = s;
+      for (int64_t e = 0; e < cnt; ++e) {
+        volatile float prod = load_elem_f(x, dtype, base + e) * inv;
+        float r = rintf(prod);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        codes[base + e] = (int8_t)r;
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * Per-block FP8 E4M3 codes ("FP8 PV", same table): as the INT8 quantiser but
+ * scale = amax / 448, inv = 448 / amax, y = clamp(x * inv, -448, 448),
+ * code = E4M3(y) rounded to nearest even. amax == 0 gives scale 0, codes 0.
+ */
+int oracle_quant_e4m3(const void* x, int dtype, int64_t BH, int N, int D,
+                      uint8_t* codes, float* scales) {
+  if (BH < 1 || N < 1 || D < 1) return -1;
+  int nblk = (N + 63) / 64;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    for (int t = 0; t < nblk; ++t) {
+      int r0 = 64 * t, r1 = r0 + 64 < N ? r0 + 64 : N;
+      int64_t base = (bh * N + r0) * (int64_t)D;
+      int64_t cnt = (int64_t)(r1 - r0) * D;
+      float amax = 0.0f;
+      for (int64_t e = 0; e < cnt; ++e) {
+        float a = fabsf(load_elem_f(x, dtype, base + e));
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) {
+        scales[bh * nblk + t] = 0.0f;
+        for (int64_t e = 0; e < cnt; ++e) codes[base + e] = 0;
+        continue;
+      }
+      volatile float s = amax / 448.0f;
+      volatile float inv = 448.0f / amax;
+      scales[bh * nblk + t] = s;
+      for (int64_t e = 0; e < cnt; ++e) {
+        volatile float y = load_elem_f(x, dtype, base + e) * inv;
+        float yc = y;
+        if (yc > 448.0f) yc = 448.0f;
+        if (yc < -448.0f) yc = -448.0f;
+        codes[base + e] = oracle_e4m3_encode(yc);
+      }
+    }
+  }
+  return 0;
+}
+
+/* -------------------------------------------- quantised-mode emulation -- */
+
+static int dequant_int8(const void* x, int dtype, int64_t BH, int N, int D, double* out) {
+  int64_t n = BH * (int64_t)N * D;
+  int nblk = (N + 63) / 64;
+  int8_t* c = (int8_t*)malloc((size_t)n);
+  float* s = (float*)malloc(sizeof(float) * (size_t)(BH * nblk));
+  if (!c || !s) { free(c); free(s); return -1; }
+  oracle_quant_int8(x, dtype, BH, N, D, c, s);
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t bh = e / ((int64_t)N * D);
+    int tok = (int)((e / D) % N);
+    out[e] = (double)c[e] * (double)s[bh * nblk + tok / 64];
+  }
+  free(c); free(s);
+  return 0;
+}
+
+static int dequant_e4m3(const void* x, int dtype, int64_t BH, int N, int D, double* out) {
+  int64_t n = BH * (int64_t)N * D;
+  int nblk = (N + 63) / 64;
+  uint8_t* c = (uint8_t*)malloc((size_t)n);
+  float* s = (float*)malloc(sizeof(float) * (size_t)(BH * nblk));
+  if (!c || !s) { free(c); free(s); return -1; }
+  oracle_quant_e4m3(x, dtype, BH, N, D, c, s);
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t bh = e / ((int64_t)N * D);
+    int tok = (int)((e / D) % N);
+    out[e] = (double)oracle_e4m3_decode(c[e]) * (double)s[bh * nblk + tok / 64];
+  }
+  free(c); free(s);
+  return 0;
+}
+
+/*
+ * Quantised-mode emulation, a diagnostic for the INT8-QK / FP8-PV recipe of
+ * the table in section 1 of "Attention kernels on a home RTX 5080": exact
+ * attention (same arguments as oracle_attn) on Q^, K^ (INT8 blocks) and V^
+ * (E4M3 blocks), where every softmax weight p_j = exp(s_j - m) of the final
+ * row max m is replaced by E4M3(fp32(448 p_j)) / 448 in the weighted sum of V
+ * while the denominator keeps the unquantised sum of p_j.
+ */
+int oracle_attn_quant(const void* q, const void* k, const void* v, int dtype,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                      int causal, int window_lo, int pos0, double scale,
+                      const int64_t* rows, int64_t nrows,
+                      double* out, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+  double* qh = (double*)malloc(sizeof(double) * (size_t)nq);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* vh = (double*)malloc(sizeof(double) * (size_t)nk);
+  int rc = -1;
+  if (qh && kh && vh &&
+      dequant_int8(q, dtype, (int64_t)B * Hq, Nq, D, qh) == 0 &&
+      dequant_int8(k, dtype, (int64_t)B * Hkv, Nk, D, kh) == 0 &&
+      dequant_e4m3(v, dtype, (int64_t)B * Hkv, Nk, D, vh) == 0) {
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+    J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale;
+    J.rows = rows;
+    J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+    J.out = out;
+    J.qhat = qh; J.khat = kh; J.vhat = vh; J.quant_p = 1;
+    rc = run_attn(&J, nthreads);
+  }
+  free(qh); free(kh); free(vh);
+  return rc;
+}

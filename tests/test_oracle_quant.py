@@ -1,0 +1,210 @@
+"""Pins for the oracle's quantisers and E4M3 codec (CPU only).
+
+Checked against the OCP E4M3 definition (named values, exhaustive round
+trips, tie rules), torch's own float8_e4m3fn cast (a library routine), closed
+forms of the symmetric INT8 quantiser (integer and half-integer blocks,
+power-of-two scaling, sign symmetry, the amax element mapping to +-127), and
+the page's printed error of the INT8-QK / FP8-PV recipe.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scaled_dot_product_amd.inputs import Workload, make_qkv, normal, sample_rows
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _e4m3_named():
+    out = []
+    with open(os.path.join(GOLDEN, "e4m3_ocp_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                val, code = line.split()
+                out.append((float(val), int(code, 16)))
+    return out
+
+
+@pytest.mark.parametrize("val,code", _e4m3_named())
+def test_e4m3_named_values(val, code):
+    assert oracle.e4m3_encode(val) == code
+    dec = oracle.e4m3_decode(code)
+    assert dec == val and math.copysign(1.0, dec) == math.copysign(1.0, val)
+
+
+def test_e4m3_nan_codes():
+    assert math.isnan(oracle.e4m3_decode(0x7F))
+    assert math.isnan(oracle.e4m3_decode(0xFF))
+
+
+def test_e4m3_round_trip_every_code():
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c
+
+
+def test_e4m3_midpoints_tie_to_even():
+    mags = sorted({abs(oracle.e4m3_decode(c)) for c in range(0x7F)})
+    for a, b in zip(mags[:-1], mags[1:]):
+        mid = (a + b) / 2.0  # exact in fp32 (one more mantissa bit)
+        ca, cb = oracle.e4m3_encode(a), oracle.e4m3_encode(b)
+        want = ca if ca % 2 == 0 else cb
+        assert oracle.e4m3_encode(mid) == want
+        assert oracle.e4m3_encode(-mid) == want | 0x80
+        # just off the midpoint goes to the nearer side
+        assert oracle.e4m3_encode(np.nextafter(np.float32(mid), np.float32(0))) == ca
+        assert oracle.e4m3_encode(np.nextafter(np.float32(mid), np.float32(1e9))) == cb
+
+
+def test_e4m3_matches_torch_float8_cast():
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch has no float8_e4m3fn")
+    g = np.random.default_rng(5)
+    vals = np.concatenate([
+        np.arange(-448 * 64, 448 * 64 + 1) / 64.0,
+        g.uniform(-448, 448, 4000),
+        g.standard_normal(4000) * 0.01,
+        np.ldexp(g.uniform(-1, 1, 2000), -8),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([oracle.e4m3_encode(float(x)) for x in vals], dtype=np.uint8)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_int8_integer_block_is_identity():
+    # amax 127 gives scale = inv = 1, so integer inputs are their own codes
+    x = torch.arange(-127, 129, dtype=torch.float32)[:256].clamp(-127, 127)
+    x = x.reshape(1, 64, 4)
+    codes, scales = oracle.quant_int8(x)
+    assert scales.tolist() == [[1.0]]
+    np.testing.assert_array_equal(codes.astype(np.float32), x.numpy())
+
+
+def test_int8_half_integers_round_to_even():
+    half = torch.tensor([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.0])
+    x = torch.zeros(1, 64, 8)
+    x[0, 0] = half
+    codes, scales = oracle.quant_int8(x)
+    assert scales[0, 0] == 1.0
+    assert codes[0, 0].tolist() == [0, 2, 2, 0, -2, -2, 126, 127]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_int8_properties_on_random_blocks(dtype):
+    x = normal((3, 200, 32), 11, dtype)      # 4 blocks per head, last holds 8 tokens
+    codes, scales = oracle.quant_int8(x)
+    assert codes.shape == (3, 200, 32) and scales.shape == (3, 4)
+    xf = x.float().numpy()
+    for h in range(3):
+        for t in range(4):
+            blk = xf[h, 64 * t:64 * t + 64]
+            cb = codes[h, 64 * t:64 * t + 64].astype(np.int32)
+            amax = np.float32(np.abs(blk).max())
+            assert scales[h, t] == np.float32(amax / np.float32(127))
+            assert np.abs(cb).max() == 127 and np.all(np.abs(cb) <= 127)
+            # the amax element maps to +-127 with its sign
+            idx = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+            assert cb[idx] == (127 if blk[idx] > 0 else -127)
+            err = np.abs(blk.astype(np.float64) - cb * np.float64(scales[h, t]))
+            # half a step, plus the fp32 rounding of x*inv (|x*inv| <= 127)
+            assert err.max() <= scales[h, t] * (0.5 + 2 ** -12)
+
+
+def test_int8_sign_symmetry_and_power_of_two_scaling():
+    x = normal((2, 130, 16), 12, torch.float32)
+    c0, s0 = oracle.quant_int8(x)
+    c1, s1 = oracle.quant_int8(-x)
+    np.testing.assert_array_equal(c1, -c0)
+    np.testing.assert_array_equal(s1, s0)
+    c2, s2 = oracle.quant_int8(x * 8.0)
+    np.testing.assert_array_equal(c2, c0)
+    np.testing.assert_array_equal(s2, s0 * 8.0)
+
+
+def test_blocks_are_independent_and_zero_block():
+    x = normal((1, 192, 8), 13, torch.float32)
+    x[0, 64:128] = 0.0
+    c0, s0 = oracle.quant_int8(x)
+    assert s0[0, 1] == 0.0 and np.all(c0[0, 64:128] == 0)
+    e0, es0 = oracle.quant_e4m3(x)
+    assert es0[0, 1] == 0.0 and np.all(e0[0, 64:128] == 0)
+    y = x.clone()
+    y[0, 150] *= 3.0
+    c1, s1 = oracle.quant_int8(y)
+    np.testing.assert_array_equal(c1[0, :128], c0[0, :128])
+    np.testing.assert_array_equal(s1[0, :2], s0[0, :2])
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_e4m3_quantiser_properties(dtype):
+    x = normal((2, 100, 64), 14, dtype)
+    codes, scales = oracle.quant_e4m3(x)
+    xf = x.float().numpy()
+    for h in range(2):
+        for t in range(2):
+            blk = xf[h, 64 * t:64 * t + 64]
+            amax = np.float32(np.abs(blk).max())
+            assert scales[h, t] == np.float32(amax / np.float32(448))
+            inv = np.float32(np.float32(448) / amax)
+            y = np.clip((blk * inv).astype(np.float32), -448, 448)
+            # codes equal torch's float8 cast of the clamped scaled block
+            ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            np.testing.assert_array_equal(codes[h, 64 * t:64 * t + 64], ref)
+            # the amax element saturates to the largest finite magnitude
+            idx = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+            assert codes[h, 64 * t + idx[0], idx[1]] & 0x7F == 0x7E
+
+
+def test_quant_emulation_uniform_scores_closed_form():
+    # Q = 0: Q's block amax is 0, so every score is 0 and every weight is 1,
+    # which E4M3 holds exactly at scale 448: the output is the mean of V^.
+    w = Workload("x", 1, 1, 1, 8, 70, 32, torch.bfloat16, causal=True, pos0=40, window_lo=5)
+    _, k, v = make_qkv(w)
+    q = torch.zeros(w.q_shape, dtype=torch.bfloat16)
+    o = oracle.attn_quant(q, k, v, scale=w.scale, causal=True, pos0=40, window_lo=5)
+    vc, vs = oracle.quant_e4m3(v)
+    dec = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    vhat = dec[vc[0, 0]] * np.repeat(vs[0, 0].astype(np.float64), 64)[:70, None]
+    for i in range(8):
+        np.testing.assert_allclose(o[0, 0, i], vhat[5:41 + i].mean(axis=0), atol=1e-13)
+
+
+def test_quant_emulation_exact_inputs_closed_form():
+    # integer Q, K with amax 127 and V of E4M3 values with amax 448 are their own
+    # codes; scores differ by multiples of ln 2 (to fp32 rounding of the scale),
+    # so every 448 * p_j is 448 * 2^-n up to rounding and E4M3 keeps it exactly.
+    D, Nk = 4, 6
+    q = torch.zeros(1, 1, 1, D)
+    q[0, 0, 0, 0] = 127.0
+    k = torch.zeros(1, 1, Nk, D)
+    k[0, 0, :, 0] = torch.tensor([1.0, 0.0, -1.0, -2.0, 1.0, 0.0])
+    k[0, 0, 0, 1] = 127.0   # make K's amax 127 without touching the scores
+    v = torch.zeros(1, 1, Nk, D)
+    v[0, 0, :, 0] = torch.tensor([448.0, 2.0, -3.0, 0.5, 1.0, -8.0])
+    scale = math.log(2.0) / 127.0
+    o = oracle.attn_quant(q, k, v, scale=scale)
+    p = np.array([2.0 ** n for n in (0, -1, -2, -3, 0, -1)])
+    s = np.array([1.0, 0.0, -1.0, -2.0, 1.0, 0.0]) * 127 * scale
+    l = np.exp(s - s.max()).sum()
+    want = (p * v[0, 0, :, 0].double().numpy()).sum() / l
+    assert abs(o[0, 0, 0, 0] - want) < 1e-6 * abs(want)
+
+
+def test_quant_emulation_error_matches_page_figure():
+    with open(os.path.join(GOLDEN, "page_error_figures.json")) as f:
+        fig = json.load(f)
+    lo, hi = fig["band_used_in_tests"]
+    w = Workload("x", 1, 1, 1, 4096, 4096, 128, torch.bfloat16)
+    q, k, v = make_qkv(w)
+    rows = sample_rows(w, 128)
+    ex = oracle.attn(q, k, v, scale=w.scale, rows=rows)
+    qe = oracle.attn_quant(q, k, v, scale=w.scale, rows=rows)
+    err = np.linalg.norm(qe - ex) / np.linalg.norm(ex)
+    assert lo <= err <= hi, err
