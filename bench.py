@@ -1,0 +1,275 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one attention forward of the video-DiT workload (B=1, 40 heads,
+32760 tokens, head dim 128, bf16, non-causal) — the shape on which the table
+in section 1 of "Attention kernels on a home RTX 5080" times its kernels. The
+same run also measures the other shapes of the hot path: the few-row GQA
+decode (cold K/V, rotated over 48 caches so the 256 MB Infinity Cache cannot
+hold them), the quantised INT8-QK / FP8-PV mode on the video shape and the
+SDXL 1024px shape. It prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Timing: HIP events on the stream the kernels are launched on (torch's current
+stream, which the binding hands to the library), around K back-to-back steps
+after W untimed ones. Decode calls are a few microseconds each, so they are
+captured in a HIP graph and the graph replay is timed. The CPU baseline times
+the fp64 oracle on a bounded sample of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 / int8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "attention fwd TFLOPS (%bf16 MFMA peak) at 40×32760×128; decode µs + HBM GB/s"
+# The pages' number for this workload and metric: PyTorch SDPA, 511 ms on an
+# RTX 5080 for 1 x 40 x 32760 x 128 bf16 (4*B*H*N*N*D flops -> 43.0 TFLOP/s).
+PAGE_SDPA_TFLOPS = 4 * 40 * 32760 * 32760 * 128 / 0.511 / 1e12
+
+
+_INPUTS = {}
+
+
+def inputs(w):
+    """Seeded CPU inputs of w, generated once per shape and dtype in this run."""
+    from scaled_dot_product_amd.inputs import make_qkv
+    key = (w.q_shape, w.kv_shape, w.dtype)
+    if key not in _INPUTS:
+        _INPUTS[key] = make_qkv(w)
+    return _INPUTS[key]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_events(fn, iters, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters  # ms
+
+
+def bench_prefill(w, steps, warmup):
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import make_qkv
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs(w))
+    out = torch.empty_like(q)
+    ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                    window_lo=w.window_lo, pos0=w.pos0, mode=w.mode,
+                                    dtype=w.dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                 scale=w.scale, mode=w.mode, out=out, workspace=ws)
+
+    ms = time_events(step, steps, warmup)
+    del q, k, v, out, ws
+    return ms
+
+
+def bench_quant_prep(w, iters=5):
+    """Time of the standalone quantisers on the same inputs (preparation share)."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import make_qkv
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs(w))
+
+    def prep():
+        sdpa.quantize_qk(q, k)
+        sdpa.quantize_v(v)
+
+    return time_events(prep, iters, 2)
+
+
+def bench_decode(w, nbuf=48, reps=20):
+    """Cold-cache decode: nbuf independent KV caches, one call per cache, captured
+    in a HIP graph; returns (us per call cold, us per call hot, bytes per call)."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import make_qkv
+    dev = torch.device("cuda:0")
+    q0, k0, v0 = (t.to(dev) for t in make_qkv(w))
+    # nbuf copies at distinct addresses: together larger than every cache level
+    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nbuf)]
+    ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                    window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        q, k, v, o = sets[i]
+        sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, scale=w.scale,
+                 out=o, workspace=ws)
+
+    for i in range(nbuf):
+        call(i)
+    torch.cuda.synchronize()
+    results = {}
+    for label, order in (("cold", list(range(nbuf))), ("hot", [0] * nbuf)):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(order[0])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in order:
+                call(i)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        results[label] = e0.elapsed_time(e1) * 1e3 / (reps * len(order))
+        del g
+    # algorithmic bytes: K and V rows of the visible keys, Q in, O out
+    lo = w.window_lo
+    hi = min(w.Nk, w.pos0 + w.Nq) if w.causal else w.Nk
+    nbytes = 2 * w.B * w.Hkv * (hi - lo) * w.D * 2 + 2 * w.B * w.Hq * w.Nq * w.D * 2
+    return results["cold"], results["hot"], nbytes
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle as it stands, on a bounded sample of rows of w (host cores)."""
+    import numpy as np
+    import oracle
+    from scaled_dot_product_amd.inputs import make_qkv, sample_rows
+    q, k, v = inputs(w)
+    threads = oracle.default_threads()
+    rows_all = sample_rows(w, 4096, seed=11)
+    done, t_used, n = 0, 0.0, threads
+    while t_used < budget_s and done < rows_all.size:
+        chunk = rows_all[done:done + n]
+        t0 = time.perf_counter()
+        oracle.attn(q, k, v, scale=w.scale, causal=w.causal, window_lo=w.window_lo,
+                    pos0=w.pos0, rows=chunk, nthreads=threads)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        done += chunk.size
+        n = min(4 * n, max(threads, int(chunk.size * (budget_s - t_used) / max(dt, 1e-3))))
+    flops = done * 4.0 * w.Nk * w.D   # non-causal rows: every key visible
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} sampled query rows of {w.name} (exact fp64 attention, "
+                      f"{t_used:.1f} s; full problem extrapolates to "
+                      f"{t_used * w.B * w.Hq * w.Nq / done / 3600:.1f} h)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sdpa.load_library()
+    free, total = torch.cuda.mem_get_info()
+    log(f"device {torch.cuda.get_device_name(0)}; free HBM {free / 2**30:.1f} of {total / 2**30:.1f} GiB")
+
+    w = WORKLOADS["video_dit_bf16_32760"]
+    log(f"headline: {w.name}, {args.warmup} warmup + {args.steps} timed steps")
+    ms = bench_prefill(w, args.steps, args.warmup)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    log(f"headline: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    extra = {}
+    if not args.only_headline:
+        wq = WORKLOADS["video_dit_quant_32760"]
+        ms_q = bench_prefill(wq, max(3, args.steps // 2), 2)
+        ms_prep = bench_quant_prep(wq)
+        extra["quant"] = {"workload": wq.name, "ms_per_call": round(ms_q, 4),
+                          "tops": round(wq.flops() / (ms_q * 1e-3) / 1e12, 2),
+                          "prep_ms": round(ms_prep, 4),
+                          "kernel_tops_est": round(wq.flops() / ((ms_q - ms_prep) * 1e-3) / 1e12, 2),
+                          "frac_of_fp8_peak": round(wq.flops() / (ms_q * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        log(f"quant: {ms_q:.3f} ms/call incl. {ms_prep:.3f} ms preparation")
+        ws_ = WORKLOADS["sdxl_1024px_bf16"]
+        ms_s = bench_prefill(ws_, 50, 10)
+        extra["sdxl"] = {"workload": ws_.name, "us_per_call": round(ms_s * 1e3, 2),
+                         "tflops": round(ws_.flops() / (ms_s * 1e-3) / 1e12, 2)}
+        log(f"sdxl: {ms_s * 1e3:.1f} us/call")
+        for wlo in (0, 1000):
+            wd = WORKLOADS["gqa_decode_f16_4096"].variant(window_lo=wlo)
+            cold_us, hot_us, nbytes = bench_decode(wd)
+            key = "decode" if wlo == 0 else "decode_window1000"
+            extra[key] = {"workload": wd.name + ("" if wlo == 0 else "_window_lo1000"),
+                          "us_per_call_cold": round(cold_us, 3),
+                          "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
+                          "us_per_call_hot": round(hot_us, 3),
+                          "bytes_per_call": nbytes,
+                          "frac_of_hbm_peak_cold": round(nbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            log(f"{key}: cold {cold_us:.2f} us ({extra[key]['gbs_cold']} GB/s), hot {hot_us:.2f} us")
+
+    cpu = None if args.skip_cpu else cpu_baseline(w)
+    if cpu:
+        log(f"cpu baseline: {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGE_SDPA_TFLOPS, 3),
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16",
+        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "N": w.Nq, "D": w.D,
+                   "causal": w.causal, "global_batch": w.B, "seq_len": w.Nq,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_kernel<bf16,bf16,128,1>",
+                     "per_launch": "21.979 TFLOP (4*B*H*N*N*D)"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

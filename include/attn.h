@@ -1,0 +1,146 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation is scaled-dot-product attention, O = softmax(scale * Q K^T +
+ * mask) V, computed flash-style: K and V are streamed through on-chip memory
+ * in tiles with a running maximum and running sum, and the Nq x Nk score
+ * matrix is never stored. The pages that describe this path name it
+ * ("attention" of shape 1 x 40 heads x 32 760 tokens x 128, bf16, in the
+ * table of section 1 of "Attention kernels on a home RTX 5080") but do not
+ * write its formula; the textbook definition is used.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *   never allocates, frees or synchronises; kernels are enqueued on `stream`
+ *   (a hipStream_t; NULL = the default stream) and the call returns once they
+ *   are enqueued.
+ * - Layouts are row-major with D innermost (the "1 x 40 heads x 32 760 tokens
+ *   x 128" order of that table): Q and O are [B][Hq][Nq][D], K and V are
+ *   [B][Hkv][Nk][D], all contiguous. O has Q's element type.
+ * - Tensor pointers must be 16-byte aligned; `workspace` 256-byte aligned.
+ * - Every argument check runs before anything is enqueued: a call that
+ *   returns an error has written nothing.
+ * - Index arithmetic is 64-bit; each single dimension must fit in int.
+ * - Calls are re-entrant; overlapping calls on different streams must use
+ *   different workspaces.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* null/misaligned pointer, bad size, bad scale  */
+  ATTN_E_UNSUPPORTED = -2, /* head dim, dtype or mode this build lacks      */
+  ATTN_E_WORKSPACE = -3,   /* workspace smaller than attn_fwd_workspace_bytes */
+  ATTN_E_HIP = -4          /* the HIP runtime refused a launch              */
+} attn_status;
+
+/* Element types of Q, K, V and O. */
+typedef enum { ATTN_DT_F32 = 0, ATTN_DT_F16 = 1, ATTN_DT_BF16 = 2 } attn_dtype;
+
+/* Arithmetic mode. The default keeps full 16-bit operands; the quantised
+ * mode is opt-in, as the explicit fast-precision policy of "Shmoosh update"
+ * (section "An explicit fast-mode policy") keeps its high-fidelity default. */
+typedef enum {
+  ATTN_MODE_EXACT = 0, /* bf16/f16 matrix products, fp32 accumulation and
+                          softmax; fp32 inputs are rounded to bf16 first */
+  ATTN_MODE_QUANT = 1  /* INT8 Q K^T and FP8 (E4M3) P V with per-block
+                          scales ("SageAttention 2 INT8 QK . FP8 PV" row of
+                          the table in section 1 of "Attention kernels on a
+                          home RTX 5080"); bf16/f16 inputs only */
+} attn_mode;
+
+/*
+ * attn_fwd — one attention forward.
+ *
+ *   q, k, v, o   device tensors in the layouts above, element type `dtype`.
+ *   B, Hq, Hkv   batch, query heads, key/value heads; Hq % Hkv == 0 and query
+ *                head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *                attention, e.g. n_head=16 over n_kv=8 in the "Performance
+ *                evidence" of "perf(metal): widen four-row flash KV tiles").
+ *   Nq, Nk       query rows and keys per head (>= 1).
+ *   D            head dimension: 64 or 128.
+ *   causal       nonzero: query row i sits at absolute position pos0 + i and
+ *                sees key j only if j <= pos0 + i (bottom-right aligned when
+ *                pos0 = Nk - Nq, as in the rows=4, kv_len=4096, pos=4092
+ *                decode of that page).
+ *   window_lo    inclusive lower bound of visible keys for every row, with or
+ *                without causal (the "sliding-window lower bound" of that
+ *                page's summary); 0 = no window.
+ *   pos0         position of query row 0 (>= 0); used only when causal.
+ *   scale        multiplier of Q K^T, finite and > 0 (usually 1/sqrt(D)).
+ *   mode         attn_mode.
+ *   dtype        attn_dtype of q, k, v and o.
+ *   workspace    device scratch of at least attn_fwd_workspace_bytes(...)
+ *                bytes (may be NULL when that is 0); contents need no
+ *                initialisation and are clobbered.
+ *   stream       hipStream_t to enqueue on.
+ *
+ * A row with no visible key (window_lo > pos0 + i) is written as exact zeros.
+ * Returns ATTN_OK or a negative attn_status; nothing is enqueued on error.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o,
+             int B, int Hq, int Hkv, int Nq, int Nk, int D,
+             int causal, int window_lo, int pos0, float scale, int mode,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_workspace_bytes — workspace attn_fwd needs for these arguments
+ * (same meaning as above). Host-only; never touches the GPU. Returns 0 for
+ * arguments attn_fwd would reject.
+ */
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                int causal, int window_lo, int pos0,
+                                int mode, int dtype);
+
+/*
+ * attn_quantize_qk — per-block symmetric INT8 codes of Q and K (the "INT8 QK"
+ * half of the quantised mode).
+ *
+ * A block is 64 consecutive tokens of one (batch, head) across all D
+ * channels; the last block of a head holds the remaining N % 64 tokens. Per
+ * block, in fp32 with round-to-nearest-even after every operation:
+ *   amax = max |x|; amax == 0 gives scale 0 and all-zero codes; otherwise
+ *   scale = amax / 127, inv = 127 / amax, code = clamp(rint(x * inv), -127, 127).
+ * Dequantisation is code * scale.
+ *
+ *   q, k          device inputs [B][Hq][Nq][D] and [B][Hkv][Nk][D], bf16/f16.
+ *   q_codes       device int8 [B][Hq][Nq][D]; k_codes [B][Hkv][Nk][D].
+ *   q_scales      device fp32 [B][Hq][ceil(Nq/64)]; k_scales [B][Hkv][ceil(Nk/64)].
+ * Codes and scales are bit-exact with the CPU oracle's definition.
+ */
+int attn_quantize_qk(const void* q, const void* k, int8_t* q_codes, float* q_scales,
+                     int8_t* k_codes, float* k_scales,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype,
+                     void* stream);
+
+/*
+ * attn_quantize_v — per-block FP8 codes of V (the "FP8 PV" half). Blocks as
+ * above; scale = amax / 448, inv = 448 / amax, y = clamp(x * inv, -448, 448),
+ * code = OCP FP8 E4M3 of y rounded to nearest even (sign kept, subnormals
+ * kept, 448 = 0x7E the largest magnitude). amax == 0 gives scale 0, codes 0.
+ *
+ *   v          device input [B][Hkv][Nk][D], bf16/f16.
+ *   v_codes    device uint8 [B][Hkv][Nk][D].
+ *   v_scales   device fp32 [B][Hkv][ceil(Nk/64)].
+ */
+int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales,
+                    int B, int Hkv, int Nk, int D, int dtype, void* stream);
+
+/* Static English text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

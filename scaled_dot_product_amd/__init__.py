@@ -1,0 +1,148 @@
+"""Fused attention forward for MI355X (gfx950) — thin Python binding.
+
+This module only marshals arguments into the C ABI of ``libattn.so``
+(declared in ``include/attn.h``): it takes device pointers from torch tensors,
+allocates the output and the workspace with torch (device memory is the only
+thing torch is used for here, besides streams), and raises on any non-zero
+status. Every step of the computation runs in the HIP kernels; there is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fwd", "fwd_workspace_bytes", "quantize_qk", "quantize_v", "load_library",
+           "MODE_EXACT", "MODE_QUANT", "AttnError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+MODE_EXACT = 0
+MODE_QUANT = 1
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def load_library():
+    """Load libattn.so (build it with ``scaled_dot_product_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise AttnError(f"{LIB_PATH} is not built; run python scaled_dot_product_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, f, vp, sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
+    lib.attn_fwd_workspace_bytes.restype = sz
+    lib.attn_quantize_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.attn_quantize_qk.restype = i
+    lib.attn_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    lib.attn_quantize_v.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().attn_status_string(status).decode()
+        raise AttnError(f"{what}: status {status} ({msg})")
+
+
+def _stream_handle(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise AttnError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise AttnError(f"{name} must be contiguous")
+    return t
+
+
+def fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos0=0,
+                        mode=MODE_EXACT, dtype=torch.bfloat16) -> int:
+    return int(load_library().attn_fwd_workspace_bytes(
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), int(mode),
+        _DTYPE[dtype]))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, window_lo=0,
+        pos0=0, scale=None, mode=MODE_EXACT, out=None, workspace=None) -> torch.Tensor:
+    """O = softmax(scale * Q K^T + mask) V on the current stream.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; one dtype (fp32, f16, bf16).
+    Returns O [B, Hq, Nq, D] in q's dtype (written into ``out`` if given).
+    """
+    lib = load_library()
+    _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise AttnError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nk,D]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise AttnError("q, k, v must share one dtype among float32, float16, bfloat16")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, Dk = k.shape
+    if Dk != D or k.shape[0] != B:
+        raise AttnError("q and k disagree on B or D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise AttnError("out must match q's shape and dtype")
+    need = fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal=causal, window_lo=window_lo,
+                               pos0=pos0, mode=mode, dtype=q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo), int(pos0),
+                      float(scale), int(mode), _DTYPE[q.dtype], ws_ptr, ws_len,
+                      _stream_handle(q))
+    _check(st, "attn_fwd")
+    return out
+
+
+def quantize_qk(q: torch.Tensor, k: torch.Tensor):
+    """Per-64-token-block INT8 codes + fp32 scales of Q and K (bf16/f16 input)."""
+    lib = load_library()
+    _dev(q, "q"), _dev(k, "k")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    qc = torch.empty(q.shape, dtype=torch.int8, device=q.device)
+    kc = torch.empty(k.shape, dtype=torch.int8, device=k.device)
+    qs = torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32, device=q.device)
+    ks = torch.empty((B, Hkv, (Nk + 63) // 64), dtype=torch.float32, device=k.device)
+    st = lib.attn_quantize_qk(q.data_ptr(), k.data_ptr(), qc.data_ptr(), qs.data_ptr(),
+                              kc.data_ptr(), ks.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+                              _DTYPE.get(q.dtype, -1), _stream_handle(q))
+    _check(st, "attn_quantize_qk")
+    return qc, qs, kc, ks
+
+
+def quantize_v(v: torch.Tensor):
+    """Per-64-token-block E4M3 codes (uint8) + fp32 scales of V (bf16/f16 input)."""
+    lib = load_library()
+    _dev(v, "v")
+    B, Hkv, Nk, D = v.shape
+    vc = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    vs = torch.empty((B, Hkv, (Nk + 63) // 64), dtype=torch.float32, device=v.device)
+    st = lib.attn_quantize_v(v.data_ptr(), vc.data_ptr(), vs.data_ptr(), B, Hkv, Nk, D,
+                             _DTYPE.get(v.dtype, -1), _stream_handle(v))
+    _check(st, "attn_quantize_v")
+    return vc, vs

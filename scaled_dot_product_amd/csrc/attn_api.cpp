@@ -1,0 +1,212 @@
+// attn_api.cpp — the C ABI declared in include/attn.h: argument checks,
+// workspace planning and kernel dispatch. Every check runs before anything is
+// enqueued, and none of them touches the HIP runtime, so a rejected call has
+// no effect on the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.hpp"
+
+namespace attn {
+
+KeyRange key_range(const FwdArgs& a) {
+  KeyRange r;
+  r.lo = a.window_lo;
+  r.hi = a.causal ? (int)(a.pos0 + (int64_t)a.Nq < a.Nk ? a.pos0 + a.Nq : a.Nk) : a.Nk;
+  if (r.hi < r.lo) r.hi = r.lo;
+  return r;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1) return ATTN_E_INVALID;
+  if (Hq % Hkv != 0) return ATTN_E_INVALID;
+  if (dtype != ATTN_DT_F32 && dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_E_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int window_lo,
+              int pos0, float scale, int mode, int dtype) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (window_lo < 0 || pos0 < 0) return ATTN_E_INVALID;
+  if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_E_INVALID;
+  if (mode != ATTN_MODE_EXACT && mode != ATTN_MODE_QUANT) return ATTN_E_UNSUPPORTED;
+  if (mode == ATTN_MODE_QUANT && dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int elem_size(int dtype) { return dtype == ATTN_DT_F32 ? 4 : 2; }
+
+FwdArgs make_args(const void* q, const void* k, const void* v, void* o, int B, int Hq,
+                  int Hkv, int Nq, int Nk, int D, int causal, int window_lo, int pos0,
+                  float scale) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
+  a.causal = causal ? 1 : 0; a.window_lo = window_lo; a.pos0 = pos0;
+  a.scale = scale;
+  // Kept a normal float so that masked scores (-inf) times c stay -inf.
+  a.c = fmaxf(scale * kLog2eHost, 1.17549435e-38f);
+  return a;
+}
+
+// Workspace layout of one call. Offsets are 256-byte aligned.
+struct Layout {
+  size_t bf16_q = 0, bf16_k = 0, bf16_v = 0;       // fp32 inputs rounded to bf16
+  size_t qc = 0, qs = 0, kc = 0, ks = 0, vc = 0, vs = 0;  // quantised mode
+  size_t dec = 0;                                  // decode partials
+  size_t total = 0;
+  bool decode = false;
+  DecodePlan plan{};
+};
+
+Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
+  Layout L;
+  size_t off = 0;
+  const size_t nq = (size_t)a.B * a.Hq * a.Nq * a.D;
+  const size_t nk = (size_t)a.B * a.Hkv * a.Nk * a.D;
+  if (mode == ATTN_MODE_QUANT) {
+    const size_t tiles = (size_t)(a.Nk + 63) / 64;
+    L.qc = off; off = round_up(off + nq);
+    L.qs = off; off = round_up(off + (size_t)a.B * a.Hq * ((a.Nq + 63) / 64) * 4);
+    L.kc = off; off = round_up(off + nk);
+    L.ks = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 4);
+    L.vc = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 64 * a.D);
+    L.vs = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 4);
+    L.total = off;
+    return L;
+  }
+  if (dtype == ATTN_DT_F32) {
+    L.bf16_q = off; off = round_up(off + nq * 2);
+    L.bf16_k = off; off = round_up(off + nk * 2);
+    L.bf16_v = off; off = round_up(off + nk * 2);
+  }
+  if (decode_eligible(a)) {
+    L.decode = true;
+    L.plan = decode_plan(a);
+    L.dec = off; off = round_up(off + L.plan.ws_bytes);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                                int window_lo, int pos0, int mode, int dtype) {
+  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype) != ATTN_OK)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  return plan_layout(a, mode, dtype).total;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+             int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+  const Layout L = plan_layout(a, mode, dtype);
+  if (L.total > 0) {
+    if (workspace_bytes < L.total) return ATTN_E_WORKSPACE;
+    if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) != 0) return ATTN_E_INVALID;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e = hipSuccess;
+
+  if (mode == ATTN_MODE_QUANT) {
+    const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+    e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
+                          (float*)(ws + L.qs), s);
+    if (e == hipSuccess)
+      e = launch_quant_int8(k, elem, (int64_t)B * Hkv, Nk, D, (int8_t*)(ws + L.kc),
+                            (float*)(ws + L.ks), s);
+    if (e == hipSuccess)
+      e = launch_quant_e4m3(v, elem, (int64_t)B * Hkv, Nk, D, (uint8_t*)(ws + L.vc),
+                            (float*)(ws + L.vs), 1, s);
+    if (e == hipSuccess)
+      e = launch_prefill_quant(a, (const int8_t*)(ws + L.qc), (const float*)(ws + L.qs),
+                               (const int8_t*)(ws + L.kc), (const float*)(ws + L.ks),
+                               (const uint8_t*)(ws + L.vc), (const float*)(ws + L.vs), elem, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  }
+
+  int elem = dtype == ATTN_DT_F16 ? 1 : 2;
+  const bool out_f32 = dtype == ATTN_DT_F32;
+  if (out_f32) {
+    const int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+    e = launch_f32_to_bf16((const float*)q, ws + L.bf16_q, nq, s);
+    if (e == hipSuccess) e = launch_f32_to_bf16((const float*)k, ws + L.bf16_k, nk, s);
+    if (e == hipSuccess) e = launch_f32_to_bf16((const float*)v, ws + L.bf16_v, nk, s);
+    if (e != hipSuccess) return ATTN_E_HIP;
+    a.q = ws + L.bf16_q;
+    a.k = ws + L.bf16_k;
+    a.v = ws + L.bf16_v;
+  }
+  if (L.decode)
+    e = launch_decode(a, L.plan, elem, out_f32, ws + L.dec, s);
+  else
+    e = launch_prefill(a, elem, out_f32, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_quantize_qk(const void* q, const void* k, int8_t* q_codes, float* q_scales,
+                     int8_t* k_codes, float* k_scales, int B, int Hq, int Hkv, int Nq, int Nk,
+                     int D, int dtype, void* stream) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(k_codes) ||
+      ((uintptr_t)q_scales & 3u) || ((uintptr_t)k_scales & 3u))
+    return ATTN_E_INVALID;
+  const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, q_codes, q_scales, s);
+  if (e == hipSuccess) e = launch_quant_int8(k, elem, (int64_t)B * Hkv, Nk, D, k_codes, k_scales, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales, int B, int Hkv, int Nk,
+                    int D, int dtype, void* stream) {
+  int st = check_shape(B, Hkv, Hkv, 1, Nk, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (!v || !v_codes || !v_scales) return ATTN_E_INVALID;
+  if (!aligned16(v) || !aligned16(v_codes) || ((uintptr_t)v_scales & 3u)) return ATTN_E_INVALID;
+  const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+  hipError_t e = launch_quant_e4m3(v, elem, (int64_t)B * Hkv, Nk, D, v_codes, v_scales, 0,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID: return "invalid argument (null or misaligned pointer, bad size, position, window or scale)";
+    case ATTN_E_UNSUPPORTED: return "unsupported head dimension, dtype or mode";
+    case ATTN_E_WORKSPACE: return "workspace smaller than attn_fwd_workspace_bytes()";
+    case ATTN_E_HIP: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

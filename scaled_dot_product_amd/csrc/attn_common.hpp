@@ -1,0 +1,86 @@
+// attn_common.hpp — device helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions used throughout (v_mfma_*_32x32x{16,32,64}):
+//   A operand: lane l holds row (l % 32) of A, K-slots of lane half (l / 32).
+//   B operand: lane l holds column (l % 32) of B, same K-slots.
+//   C/D:       lane l, register j holds row 8*(j/4) + 4*(l/32) + (j%4),
+//              column l % 32.
+// A and B pair K-slots symmetrically, so any consistent slot -> K-index map
+// gives the same product; the kernels pick the map that keeps every operand
+// a contiguous 16-byte read.
+//
+// Scores are computed transposed, S^T = K Q^T, so that a lane owns one query
+// column: the row maximum and sum of the softmax are in-lane reductions plus
+// one exchange between the two lane halves, and the probabilities are already
+// in B-operand position for O^T += V^T P^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-bit element traits: the 8-wide operand vector and the MFMA on it.
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ __bf16 from_float(float x) { return (__bf16)x; }
+};
+template <> struct Elem<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ _Float16 from_float(float x) { return (_Float16)x; }
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Reductions across the two lane halves (lane l with lane l ^ 32) with one
+// v_permlane32_swap: with both operands x, the first result holds x of the
+// low half in every lane and the second holds x of the high half.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup id -> logical tile so that tiles [x*T/8, (x+1)*T/8) run on XCD x
+// (the dispatcher places workgroup w on XCD w % 8); neighbouring tiles, which
+// share K/V, then share one L2.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = w % 8, local = w / 8;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Key index inside a 32-key block held by C-row m of S^T: swapping bits 2 and
+// 3 makes lane half h's registers j = 8t + i hold keys 16t + 8h + i, i.e. a
+// contiguous 8-key B-operand slice for each 16-key step of P V. It is its own
+// inverse, so it also maps a key to the LDS row the kernels store it in.
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+}  // namespace attn

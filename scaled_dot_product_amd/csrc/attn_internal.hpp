@@ -1,0 +1,62 @@
+// attn_internal.hpp — host-side launch plans shared by the C ABI and the
+// kernel translation units. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Arguments of one forward call after validation.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal, window_lo, pos0;
+  float scale;
+  float c;  // scale * log2(e): scores are exponentiated with exp2
+};
+
+// Visible key range [lo, hi) over all rows of a call (hi <= lo: none).
+struct KeyRange {
+  int lo, hi;
+};
+KeyRange key_range(const FwdArgs& a);
+
+// ---- exact-mode prefill (bf16/f16 MFMA) ----------------------------------
+// elem: 1 = f16, 2 = bf16 operands; out_f32: write fp32 output.
+hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s);
+
+// ---- split-KV decode + log-sum-exp merge ---------------------------------
+struct DecodePlan {
+  int rows;       // G * Nq query rows per key/value head (<= 32)
+  int t_lo;       // first 64-key tile
+  int ntiles;     // tiles in the visible range
+  int nsplit;     // workgroups per key/value head
+  size_t ws_bytes;
+};
+bool decode_eligible(const FwdArgs& a);
+DecodePlan decode_plan(const FwdArgs& a);
+hipError_t launch_decode(const FwdArgs& a, const DecodePlan& p, int elem, bool out_f32,
+                         void* ws, hipStream_t s);
+
+// ---- fp32 inputs: rounded to bf16 before the MFMA path --------------------
+hipError_t launch_f32_to_bf16(const float* x, void* y, int64_t n, hipStream_t s);
+
+// ---- quantised mode ------------------------------------------------------
+hipError_t launch_quant_int8(const void* x, int elem, int64_t BH, int N, int D,
+                             int8_t* codes, float* scales, hipStream_t s);
+// layout 0: codes [BH][N][D]; layout 1: per 64-key tile, transposed
+// [BH][ceil(N/64)][D][64] with zero codes for keys past N.
+hipError_t launch_quant_e4m3(const void* x, int elem, int64_t BH, int N, int D,
+                             uint8_t* codes, float* scales, int layout, hipStream_t s);
+hipError_t launch_prefill_quant(const FwdArgs& a, const int8_t* qc, const float* qs,
+                                const int8_t* kc, const float* ks, const uint8_t* vct,
+                                const float* vs, int elem_out, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports every entry point include/attn.h
+declares; argument checks reject bad calls before touching the GPU (CPU only:
+no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE = 0, -1, -2, -3
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sdpa.LIB_PATH):
+        from scaled_dot_product_amd import build
+        build.build()
+    return sdpa.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
+              "attn_quantize_v", "attn_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.attn_status_string(st), bytes)
+
+
+# A fake, 256-aligned address: the checks below fail before any dereference.
+FAKE = 1 << 20
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, D=64,
+             causal=0, window_lo=0, pos0=0, scale=0.125, mode=0, dtype=2,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                        a["Nk"], a["D"], a["causal"], a["window_lo"], a["pos0"], a["scale"],
+                        a["mode"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_INVALID),
+    (dict(o=None), E_INVALID),
+    (dict(k=FAKE + 8), E_INVALID),            # misaligned
+    (dict(B=0), E_INVALID),
+    (dict(Nq=0), E_INVALID),
+    (dict(Nk=-3), E_INVALID),
+    (dict(Hq=3, Hkv=2), E_INVALID),           # Hq % Hkv != 0
+    (dict(window_lo=-1), E_INVALID),
+    (dict(pos0=-5, causal=1), E_INVALID),
+    (dict(scale=0.0), E_INVALID),
+    (dict(scale=-0.1), E_INVALID),
+    (dict(scale=float("nan")), E_INVALID),
+    (dict(scale=float("inf")), E_INVALID),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(D=256), E_UNSUPPORTED),
+    (dict(dtype=7), E_UNSUPPORTED),
+    (dict(mode=5), E_UNSUPPORTED),
+    (dict(mode=1, dtype=0), E_UNSUPPORTED),   # quantised mode needs 16-bit inputs
+    (dict(dtype=0), E_WORKSPACE),             # fp32 inputs need a bf16 staging workspace
+    (dict(mode=1), E_WORKSPACE),
+])
+def test_fwd_rejects_before_enqueue(lib, kw, want):
+    assert _fwd(lib, **kw) == want
+
+
+def test_workspace_misaligned_rejected(lib):
+    need = lib.attn_fwd_workspace_bytes(1, 2, 2, 8, 8, 64, 0, 0, 0, 0, 0)
+    assert need > 0
+    assert _fwd(lib, dtype=0, ws=FAKE + 16, ws_bytes=need) == E_INVALID
+
+
+def test_workspace_bytes(lib):
+    ws = lib.attn_fwd_workspace_bytes
+    # exact bf16 prefill needs none; decode, fp32 staging and quant mode do
+    assert ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 0, 2) == 0
+    assert ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0, 1) > 0
+    assert ws(1, 2, 2, 256, 256, 64, 0, 0, 0, 0, 0) >= 3 * 2 * 256 * 64 * 2
+    q = ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 1, 2)
+    assert q >= 3 * 40 * 32760 * 128
+    # rejected arguments report 0
+    assert ws(1, 3, 2, 8, 8, 64, 0, 0, 0, 0, 2) == 0
+    assert ws(1, 2, 2, 8, 8, 96, 0, 0, 0, 0, 2) == 0
+
+
+def test_quantizers_reject_before_enqueue(lib):
+    assert lib.attn_quantize_qk(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 2, None) == E_INVALID
+    assert lib.attn_quantize_qk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 0, None) == E_UNSUPPORTED
+    assert lib.attn_quantize_qk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 2, 8, 8, 64, 2, None) == E_INVALID
+    assert lib.attn_quantize_v(FAKE, FAKE, None, 1, 2, 8, 64, 2, None) == E_INVALID
+    assert lib.attn_quantize_v(FAKE, FAKE, FAKE, 1, 2, 8, 80, 2, None) == E_UNSUPPORTED
+    assert lib.attn_quantize_v(FAKE, FAKE, FAKE, 1, 2, 0, 64, 2, None) == E_INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(sdpa.AttnError):
+        sdpa.fwd(q, q, q)
