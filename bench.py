@@ -164,7 +164,7 @@ def cpu_baseline(w, budget_s=12.0):
     from scaled_dot_product_amd.inputs import make_qkv, sample_rows
     q, k, v = inputs(w)
     threads = oracle.default_threads()
-    rows_all = sample_rows(w, 4096, seed=11)
+    rows_all = sample_rows(w, 32768, seed=11)
     done, t_used, n = 0, 0.0, threads
     while t_used < budget_s and done < rows_all.size:
         chunk = rows_all[done:done + n]
@@ -183,6 +183,41 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{t_used * w.B * w.Hq * w.Nq / done / 3600:.1f} h)"}
 
 
+def run_extra(part):
+    from scaled_dot_product_amd.inputs import WORKLOADS
+    extra = {}
+    if part == "quant":
+        wq = WORKLOADS["video_dit_quant_32760"]
+        ms_q = bench_prefill(wq, 10, 2)
+        ms_prep = bench_quant_prep(wq)
+        extra["quant"] = {"workload": wq.name, "ms_per_call": round(ms_q, 4),
+                          "tops": round(wq.flops() / (ms_q * 1e-3) / 1e12, 2),
+                          "prep_ms": round(ms_prep, 4),
+                          "kernel_tops_est": round(wq.flops() / ((ms_q - ms_prep) * 1e-3) / 1e12, 2),
+                          "frac_of_fp8_peak": round(wq.flops() / (ms_q * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        log(f"quant: {ms_q:.3f} ms/call incl. {ms_prep:.3f} ms preparation")
+    elif part == "sdxl":
+        ws_ = WORKLOADS["sdxl_1024px_bf16"]
+        ms_s = bench_prefill(ws_, 50, 10)
+        extra["sdxl"] = {"workload": ws_.name, "us_per_call": round(ms_s * 1e3, 2),
+                         "tflops": round(ws_.flops() / (ms_s * 1e-3) / 1e12, 2),
+                         "frac_of_bf16_peak": round(ws_.flops() / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"sdxl: {ms_s * 1e3:.1f} us/call")
+    elif part == "decode":
+        for wlo in (0, 1000):
+            wd = WORKLOADS["gqa_decode_f16_4096"].variant(window_lo=wlo)
+            cold_us, hot_us, nbytes = bench_decode(wd)
+            key = "decode" if wlo == 0 else "decode_window1000"
+            extra[key] = {"workload": wd.name + ("" if wlo == 0 else "_window_lo1000"),
+                          "us_per_call_cold": round(cold_us, 3),
+                          "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
+                          "us_per_call_hot": round(hot_us, 3),
+                          "bytes_per_call": nbytes,
+                          "frac_of_hbm_peak_cold": round(nbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            log(f"{key}: cold {cold_us:.2f} us ({extra[key]['gbs_cold']} GB/s), hot {hot_us:.2f} us")
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +225,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
+    ap.add_argument("--only", choices=["decode", "quant", "sdxl"],
+                    help="time one secondary workload only (for kernel profiles)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -207,6 +244,11 @@ def main():
     free, total = torch.cuda.mem_get_info()
     log(f"device {torch.cuda.get_device_name(0)}; free HBM {free / 2**30:.1f} of {total / 2**30:.1f} GiB")
 
+    if args.only:
+        extra = run_extra(args.only)
+        print(json.dumps({"only": args.only, "extra": extra}), flush=True)
+        return
+
     w = WORKLOADS["video_dit_bf16_32760"]
     log(f"headline: {w.name}, {args.warmup} warmup + {args.steps} timed steps")
     ms = bench_prefill(w, args.steps, args.warmup)
@@ -215,31 +257,8 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        wq = WORKLOADS["video_dit_quant_32760"]
-        ms_q = bench_prefill(wq, max(3, args.steps // 2), 2)
-        ms_prep = bench_quant_prep(wq)
-        extra["quant"] = {"workload": wq.name, "ms_per_call": round(ms_q, 4),
-                          "tops": round(wq.flops() / (ms_q * 1e-3) / 1e12, 2),
-                          "prep_ms": round(ms_prep, 4),
-                          "kernel_tops_est": round(wq.flops() / ((ms_q - ms_prep) * 1e-3) / 1e12, 2),
-                          "frac_of_fp8_peak": round(wq.flops() / (ms_q * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        log(f"quant: {ms_q:.3f} ms/call incl. {ms_prep:.3f} ms preparation")
-        ws_ = WORKLOADS["sdxl_1024px_bf16"]
-        ms_s = bench_prefill(ws_, 50, 10)
-        extra["sdxl"] = {"workload": ws_.name, "us_per_call": round(ms_s * 1e3, 2),
-                         "tflops": round(ws_.flops() / (ms_s * 1e-3) / 1e12, 2)}
-        log(f"sdxl: {ms_s * 1e3:.1f} us/call")
-        for wlo in (0, 1000):
-            wd = WORKLOADS["gqa_decode_f16_4096"].variant(window_lo=wlo)
-            cold_us, hot_us, nbytes = bench_decode(wd)
-            key = "decode" if wlo == 0 else "decode_window1000"
-            extra[key] = {"workload": wd.name + ("" if wlo == 0 else "_window_lo1000"),
-                          "us_per_call_cold": round(cold_us, 3),
-                          "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
-                          "us_per_call_hot": round(hot_us, 3),
-                          "bytes_per_call": nbytes,
-                          "frac_of_hbm_peak_cold": round(nbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-            log(f"{key}: cold {cold_us:.2f} us ({extra[key]['gbs_cold']} GB/s), hot {hot_us:.2f} us")
+        for part in ("quant", "sdxl", "decode"):
+            extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)
     if cpu:

@@ -38,6 +38,9 @@ struct DecodePlan {
   int t_lo;       // first 64-key tile
   int ntiles;     // tiles in the visible range
   int nsplit;     // workgroups per key/value head
+  int tiles_per_wg;
+  int waves;      // waves per workgroup (1, 2 or 4), one 64-key tile each per step
+  size_t ctr_bytes;  // arrival counters at the start of the workspace
   size_t ws_bytes;
 };
 bool decode_eligible(const FwdArgs& a);

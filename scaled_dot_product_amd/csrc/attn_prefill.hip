@@ -80,20 +80,16 @@ prefill_kernel(FwdArgs a, int ntq) {
   const int qw0 = q0 + wave * QB * 32;  // first row of this wave
 
   // Tile loads: thread -> key group kg (KPT consecutive keys) and 16-byte
-  // column cc. Keys past Nk load as zeros so masked lanes never meet NaN.
+  // column cc. Rows past Nk are clamped to the last row, so every load is
+  // unconditional (no branches between them); those keys are masked.
   const int kg = tid % KG, cc = tid / KG;
   u32x4 kreg[KPT], vreg[KPT];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int key = k0 + kg * KPT + r;
-      if (key < a.Nk) {
-        kreg[r] = ld16(Kp + (int64_t)key * D + 8 * cc);
-        vreg[r] = ld16(Vp + (int64_t)key * D + 8 * cc);
-      } else {
-        kreg[r] = u32x4{0, 0, 0, 0};
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
+      const int key = min(k0 + kg * KPT + r, a.Nk - 1);
+      kreg[r] = ld16(Kp + (int64_t)key * D + 8 * cc);
+      vreg[r] = ld16(Vp + (int64_t)key * D + 8 * cc);
     }
   };
   auto lstore = [&](int buf) {
@@ -143,23 +139,34 @@ prefill_kernel(FwdArgs a, int ntq) {
     const int k0 = t * 64;
     if (t + 1 < t_hi) gload(k0 + 64);
 
-    // S^T = K Q^T for 64 keys x 32*QB queries.
-    f32x16 s[2][QB];
+    // S^T = K Q^T for 64 keys x 32*QB queries; even and odd k-steps go to
+    // separate accumulators so that four MFMA chains are in flight.
+    f32x16 s[2][QB], s2[2][QB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[mb][qb][j] = 0.0f;
+        for (int j = 0; j < 16; ++j) s[mb][qb][j] = s2[mb][qb][j] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ks += 2) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const V8 ka = *(const V8*)&sk[buf][(32 * mb + col) * KLD + 16 * ks + 8 * half];
+        const V8 kb = *(const V8*)&sk[buf][(32 * mb + col) * KLD + 16 * ks + 16 + 8 * half];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[mb][qb] = E::mma(ka, qv[qb][ks], s[mb][qb]);
+        for (int qb = 0; qb < QB; ++qb) {
+          s[mb][qb] = E::mma(ka, qv[qb][ks], s[mb][qb]);
+          s2[mb][qb] = E::mma(kb, qv[qb][ks + 1], s2[mb][qb]);
+        }
       }
     }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[mb][qb][j] += s2[mb][qb][j];
 
     // Boundary tiles only: window edge, ragged end, causal diagonal.
     const bool need_mask = (k0 < kv_lo) || (k0 + 64 > a.Nk) ||

@@ -245,8 +245,8 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     for (int u = 0; u < KCH; ++u) {
       const int ch = tid + 256 * u;
       const int kk = ch / (D / 16), c = ch - kk * (D / 16);
-      const int key = 64 * t + kk;
-      kreg[u] = key < a.Nk ? ld16(Kc + (int64_t)key * D + 16 * c) : u32x4{0, 0, 0, 0};
+      const int key = min(64 * t + kk, a.Nk - 1);   // clamped rows are masked
+      kreg[u] = ld16(Kc + (int64_t)key * D + 16 * c);
     }
 #pragma unroll
     for (int u = 0; u < VCH; ++u) {

@@ -220,3 +220,63 @@ def test_quant_mode_zero_q_is_mean_of_vhat():
         vhat = dec[vc[0, h]] * np.repeat(vs[0, h].astype(np.float64), 64)[:300, None]
         want = vhat.mean(axis=0)
         np.testing.assert_allclose(out[0, h], np.broadcast_to(want, (64, 128)), rtol=0, atol=1e-2)
+
+
+# ---- fused decode: workspace state and graph replay --------------------------
+
+def _decode_case():
+    w = WORKLOADS["gqa_decode_f16_4096"]
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    return w, q.to(dev), k.to(dev), v.to(dev)
+
+
+def test_decode_garbage_workspace():
+    # the arrival counters live in the workspace; any prior content must work
+    w, q, k, v = _decode_case()
+    n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=True,
+                                 pos0=w.pos0, dtype=w.dtype)
+    ref = None
+    for fill in (0x00, 0xFF, 0xA5):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=q.device)
+        out = sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        if ref is None:
+            qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+            r = oracle.attn(qc, kc, vc, scale=w.scale, causal=True, pos0=w.pos0)
+            rel, _ = metrics(out.double().cpu().numpy(), r)
+            assert rel < 1e-2
+            ref = out.clone()
+        assert torch.equal(out, ref), fill
+        # the same workspace again: counters were left reset
+        out2 = sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, ref)
+
+
+def test_decode_graph_replays_match_eager():
+    w, q, k, v = _decode_case()
+    n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=True,
+                                 pos0=w.pos0, dtype=w.dtype)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    eager = sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, out=out, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), r
+        # eager work on the same workspace between replays
+        e2 = sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(e2, eager)
