@@ -28,6 +28,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -65,6 +67,36 @@ __device__ __forceinline__ float halves_sum(float x) {
                                             false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group,
+// lane 4a + e receives element e of the four 8-byte rows whose addresses
+// lanes a, a+4, a+8 and a+12 supply. The body exists only in the device pass
+// (the host pass cannot type the LDS address-space cast).
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+#else
+  (void)p;
+  return s16x4{0, 0, 0, 0};
+#endif
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16 i (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void load_to_lds16(const void* g, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#else
+  (void)g;
+  (void)lds_base;
+#endif
+}
+
+// Wait until every vector-memory operation of this wave has completed,
+// including global -> LDS loads (s_waitcnt vmcnt(0); the other counters are
+// left alone).
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup id -> logical tile so that tiles [x*T/8, (x+1)*T/8) run on XCD x
 // (the dispatcher places workgroup w on XCD w % 8); neighbouring tiles, which

@@ -1,18 +1,31 @@
 // attn_prefill.hip — exact-mode flash attention forward for gfx950.
 //
-// One workgroup of 4 waves owns BM = 4 * 32 * QB query rows of one
-// (batch, query head); each wave owns 32 * QB rows. The workgroup streams the
-// visible keys of its key/value head in tiles of 64: K and V are read from
-// HBM/L2 with 16-byte loads, staged in double-buffered LDS (K row-major, V
-// transposed), and every wave runs
+// One workgroup of 4 waves owns 128 query rows of one (batch, query head);
+// each wave owns 32 rows, two workgroups share a CU (2 waves per SIMD). The
+// workgroup streams the visible keys of its key/value head in tiles of 64:
+// K and V go from HBM/L2 straight into LDS (global_load_lds, 16 bytes per
+// lane, no register staging) in row-major tiles with an XOR swizzle of the
+// 16-byte chunks, and every wave runs
 //     S^T = K Q^T                   (bf16/f16 MFMA, fp32 accumulation)
 //     mask (boundary tiles only)
 //     online softmax in exp2 units  (running max, running sum, lazy rescale)
-//     O^T += V^T P^T                (P rounded to the operand type)
+//     O^T += V^T P^T                (P rounded to the operand type; the V^T
+//                                   operands come from the row-major V tile
+//                                   through ds_read_b64_tr_b16 transposes)
 // before the epilogue divides by the running sum. The N x N score matrix is
-// never stored. 64-key tiles follow the 64-position KV chunk of
-// "perf(metal): widen four-row flash KV tiles" (its 128-position chunk is a
-// different trade-off for a four-row shape on another GPU).
+// never stored.
+//
+// The loop is software-pipelined so the matrix cores do not wait for the
+// softmax: iteration i computes S for tile i+1 on the MFMA pipe while the
+// vector ALU exponentiates tile i, then accumulates P V for tile i. K tile
+// i+1 and V tile i are resident together, so K and V use separate LDS double
+// buffers offset by one tile, and one barrier per iteration suffices. The
+// instruction interleave inside an iteration is fixed with scheduling-group
+// barriers.
+//
+// 64-key tiles follow the 64-position KV chunk of "perf(metal): widen
+// four-row flash KV tiles" (its 128-position chunk is a different trade-off,
+// for a four-row shape on another GPU).
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
@@ -26,21 +39,23 @@ namespace {
 // denominator share the stale maximum.
 constexpr float kLazyLog2 = 8.0f;
 
-template <typename T, typename TO, int D, int QB>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+// Scheduling-group masks (see the AMDGPU backend's sched_group_barrier).
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <typename T, typename TO, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(FwdArgs a, int ntq) {
   using E = Elem<T>;
   using V8 = typename E::vec8;
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int BM = 128;
   constexpr int KS = D / 16;       // 16-wide k-steps of Q K^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
-  constexpr int KLD = D + 8;       // K tile row stride (elements): +16 B pad
-  constexpr int VLD = 64 + 8;      // V^T tile row stride (elements): +16 B pad
-  constexpr int KPT = D / 32;      // keys per thread in a tile load
-  constexpr int KG = 64 / KPT;     // key groups per tile
-  __shared__ __attribute__((aligned(16))) T sk[2][64 * KLD];
-  __shared__ __attribute__((aligned(16))) T sv[2][D * VLD];
+  constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;    // rows one 64-lane direct load covers
+  __shared__ __attribute__((aligned(16))) T sk[2][64 * D];
+  __shared__ __attribute__((aligned(16))) T sv[2][64 * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -55,200 +70,205 @@ prefill_kernel(FwdArgs a, int ntq) {
   const T* __restrict__ Vp = (const T*)a.v + kvbase;
   TO* __restrict__ Op = (TO*)a.o + (int64_t)bh * a.Nq * D;
 
-  // Visible keys of this workgroup's rows.
+  // Visible keys of this workgroup's rows, as tiles [t_lo, t_lo + nt).
   const int qlast = min(q0 + BM, a.Nq) - 1;
   const int kv_lo = a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
   const int t_lo = kv_lo / 64;
-  const int t_hi = kv_hi > kv_lo ? (kv_hi + 63) / 64 : t_lo;
+  const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
 
   // Q^T as B operands, held for the whole loop: column = query row,
   // lane half h of k-step ks holds d = 16 ks + 8 h + (0..7).
-  V8 qv[QB][KS];
-  int qrow[QB];
+  const int qrow = q0 + wave * 32 + col;
+  const int qw0 = q0 + wave * 32;  // first row of this wave
+  V8 qv[KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = q0 + (wave * QB + qb) * 32 + col;
-    const bool ok = qrow[qb] < a.Nq;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 raw = {0, 0, 0, 0};
-      if (ok) raw = ld16(Qp + (int64_t)qrow[qb] * D + 16 * ks + 8 * half);
-      qv[qb][ks] = __builtin_bit_cast(V8, raw);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 raw = {0, 0, 0, 0};
+    if (qrow < a.Nq) raw = ld16(Qp + (int64_t)qrow * D + 16 * ks + 8 * half);
+    qv[ks] = __builtin_bit_cast(V8, raw);
   }
-  const int qw0 = q0 + wave * QB * 32;  // first row of this wave
 
-  // Tile loads: thread -> key group kg (KPT consecutive keys) and 16-byte
-  // column cc. Rows past Nk are clamped to the last row, so every load is
-  // unconditional (no branches between them); those keys are masked.
-  const int kg = tid % KG, cc = tid / KG;
-  u32x4 kreg[KPT], vreg[KPT];
-  auto gload = [&](int k0) {
+  // LDS tiles are 64 unpadded rows of D elements; chunk c of row r sits at
+  // chunk position c ^ swz(r). K row r holds key (r & ~31) | swap23(r & 31)
+  // (so P^T lands in B-operand order), V row r holds key r. The swizzles make
+  // the 16 lanes of a K operand read (16 rows, one logical chunk) and the 32
+  // lanes of a V transpose read (4 rows x 8 chunks) hit distinct banks.
+  auto kswz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  // Direct loads: each wave fills 16 rows of the K and of the V tile, RPI
+  // rows per instruction (lane i -> row i / CPR, chunk position i % CPR).
+  // Rows past Nk are clamped to the last row (finite values; masked).
+  auto load_k = [&](int t, int buf) {
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int key = min(k0 + kg * KPT + r, a.Nk - 1);
-      kreg[r] = ld16(Kp + (int64_t)key * D + 8 * cc);
-      vreg[r] = ld16(Vp + (int64_t)key * D + 8 * cc);
+    for (int u = 0; u < 16 / RPI; ++u) {
+      const int r0 = 16 * wave + RPI * u;
+      const int r = r0 + lane / CPR, pos = lane % CPR;
+      const int kk = (r & ~31) | swap23(r & 31);
+      const int key = min(64 * t + kk, a.Nk - 1);
+      load_to_lds16(Kp + (int64_t)key * D + 8 * (pos ^ kswz(r)), &sk[buf][r0 * D]);
     }
   };
-  auto lstore = [&](int buf) {
+  auto load_v = [&](int t, int buf) {
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int kk = kg * KPT + r;
-      const int row = (kk & ~31) | swap23(kk & 31);
-      st16(&sk[buf][row * KLD + 8 * cc], kreg[r]);
-    }
-    // V^T: element e of every key's chunk goes to row d = 8 cc + e.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      T* dst = &sv[buf][(8 * cc + e) * VLD + kg * KPT];
-      if constexpr (KPT == 4) {
-        u32x2 pk;
-        pk[0] = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-        pk[1] = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
-        *(u32x2*)dst = pk;
-      } else {
-        *(uint32_t*)dst = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-      }
+    for (int u = 0; u < 16 / RPI; ++u) {
+      const int r0 = 16 * wave + RPI * u;
+      const int r = r0 + lane / CPR, pos = lane % CPR;
+      const int key = min(64 * t + r, a.Nk - 1);
+      load_to_lds16(Vp + (int64_t)key * D + 8 * (pos ^ vswz(r)), &sv[buf][r0 * D]);
     }
   };
 
-  f32x16 oacc[DB][QB];
+  // Boundary tiles only: window edge, ragged end, causal diagonal.
+  auto apply_mask = [&](f32x16 (&s)[2], int t) {
+    const int k0 = 64 * t;
+    const bool need = (k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0);
+    if (need) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
+          const bool vis = key >= kv_lo && key < a.Nk && (!a.causal || key <= a.pos0 + qrow);
+          if (!vis) s[mb][j] = -INFINITY;
+        }
+    }
+  };
+
+  f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][qb][j] = 0.0f;
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
-  }
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
 
-  if (t_lo < t_hi) {
-    gload(t_lo * 64);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const int k0 = t * 64;
-    if (t + 1 < t_hi) gload(k0 + 64);
-
-    // S^T = K Q^T for 64 keys x 32*QB queries; even and odd k-steps go to
-    // separate accumulators so that four MFMA chains are in flight.
-    f32x16 s[2][QB], s2[2][QB];
+  // S^T of one tile from an LDS K buffer (two independent MFMA chains).
+  auto s_mma = [&](int buf, f32x16 (&s)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int j = 0; j < 16; ++j) s[mb][j] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[mb][qb][j] = s2[mb][qb][j] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const V8 ka = *(const V8*)&sk[buf][(32 * mb + col) * KLD + 16 * ks + 8 * half];
-        const V8 kb = *(const V8*)&sk[buf][(32 * mb + col) * KLD + 16 * ks + 16 + 8 * half];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[mb][qb] = E::mma(ka, qv[qb][ks], s[mb][qb]);
-          s2[mb][qb] = E::mma(kb, qv[qb][ks + 1], s2[mb][qb]);
-        }
+        const int r = 32 * mb + col;
+        const V8 ka = *(const V8*)&sk[buf][r * D + 8 * ((2 * ks + half) ^ kswz(r))];
+        s[mb] = E::mma(ka, qv[ks], s[mb]);
       }
+  };
+
+  // One pipeline step: softmax and P V of tile i (scores in cur), S of tile
+  // i + 1 into nxt, then the stores and loads that keep K two tiles and V one
+  // tile ahead.
+  auto step = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const int t = t_lo + i;
+    // K tile i + 2 goes where K tile i was, V tile i + 1 where V tile i - 1
+    // was (both last read before the previous barrier); they land during
+    // this step and are published by its closing barrier.
+    if (i + 2 < nt) load_k(t + 2, i & 1);
+    if (i + 1 < nt) load_v(t + 1, (i + 1) & 1);
+    apply_mask(cur, t);
+    float mx = cur[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, cur[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][j]);
+    mx = halves_max(mx) * a.c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m_run = m_new;
     }
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
+
+    // S of tile i + 1 (MFMA) interleaved with the exponentials of tile i.
+    s_mma((i + 1) & 1, nxt);
+    V8 pv[2][2];
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int tt = 0; tt < 2; ++tt) {
+        V8 p;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[mb][qb][j] += s2[mb][qb][j];
-
-    // Boundary tiles only: window edge, ragged end, causal diagonal.
-    const bool need_mask = (k0 < kv_lo) || (k0 + 64 > a.Nk) ||
-                           (a.causal && k0 + 63 > a.pos0 + qw0);
-    if (need_mask) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-            const bool vis = key >= kv_lo && key < a.Nk &&
-                             (!a.causal || key <= a.pos0 + qrow[qb]);
-            if (!vis) s[mb][qb][j] = -INFINITY;
-          }
-    }
-
-    // Online softmax (exp2 units) and P^T as B operands.
-    V8 pv[QB][2][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[0][qb][j]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][qb][j]);
-      mx = halves_max(mx) * a.c;
-      const bool grow = mx > m_run[qb] + kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha =
-            m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[db][qb][j] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float mu = m_run[qb] == -INFINITY ? 0.0f : m_run[qb];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          V8 p;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][qb][8 * tt + i], a.c, -mu));
-            lsum += e;
-            p[i] = E::from_float(e);
-          }
-          pv[qb][mb][tt] = p;
+        for (int q = 0; q < 8; ++q) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(cur[mb][8 * tt + q], a.c, -mu));
+          ls[q & 3] += e;
+          p[q] = E::from_float(e);
         }
-      l_run[qb] += lsum;
+        pv[mb][tt] = p;
+      }
+    // 2*KS MFMAs with the exponentials spread between them; the K reads run
+    // two MFMAs ahead.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * KS - 2; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / KS, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
+    // O^T += V^T P^T for tile i (4 k-steps of 16 keys, DB chains). In each
+    // 16-lane group the transpose read hands lane 4a + e element e of the
+    // rows named by lanes a, a+4, a+8, a+12: lane r names key kb + r/4 at
+    // channel d0 + 4 (r % 4), so lane (col, half) gets channel col of keys
+    // kb..kb+3, i.e. four B-operand slots of P^T's order.
+    const int vb = i & 1;
+    const int gq = lane >> 4, rr = lane & 15;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const V8 va =
-              *(const V8*)&sv[buf][(32 * db + col) * VLD + 32 * mb + 16 * tt + 8 * half];
+          s16x4 part[2];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = E::mma(va, pv[qb][mb][tt], oacc[db][qb]);
+          for (int rd = 0; rd < 2; ++rd) {
+            const int key = 32 * mb + 16 * tt + 8 * (gq >> 1) + 4 * rd + (rr >> 2);
+            const int d0 = 32 * db + 16 * (gq & 1) + 4 * (rr & 3);
+            const int off = key * D + 8 * ((d0 >> 3) ^ vswz(key)) + (d0 & 7);
+            part[rd] = lds_read_tr16(&sv[vb][off]);
+          }
+          const s16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                              part[1][0], part[1][1], part[1][2], part[1][3]};
+          oacc[db] = E::mma(__builtin_bit_cast(V8, both), pv[mb][tt], oacc[db]);
         }
 
-    if (t + 1 < t_hi) lstore(buf ^ 1);
+    vmem_wait_all();   // this wave's direct-to-LDS loads have landed
     __syncthreads();
+  };
+
+  if (nt > 0) {
+    // Prologue: K tiles 0 and 1 and V tile 0 in LDS, S of tile 0.
+    load_k(t_lo, 0);
+    load_v(t_lo, 0);
+    if (nt > 1) load_k(t_lo + 1, 1);
+    vmem_wait_all();
+    __syncthreads();
+    f32x16 s0[2], s1[2];
+    s_mma(0, s0);
+    __syncthreads();   // step 0 overwrites the K buffer just read
+    int i = 0;
+    for (; i + 1 < nt; i += 2) {
+      step(i, s0, s1);
+      step(i + 1, s1, s0);
+    }
+    if (i < nt) step(i, s0, s1);
   }
 
   // Epilogue: O = O_acc / l; rows with no visible key are written as zeros.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = halves_sum(l_run[qb]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (qrow[qb] >= a.Nq) continue;
-    TO* orow = Op + (int64_t)qrow[qb] * D;
+  const float l = halves_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qrow < a.Nq) {
+    TO* orow = Op + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -257,37 +277,36 @@ prefill_kernel(FwdArgs a, int ntq) {
         if constexpr (sizeof(TO) == 4) {
           f32x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][qb][4 * a4 + r] * inv;
+          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][4 * a4 + r] * inv;
           *(f32x4*)(orow + d) = o4;
         } else {
           TO o4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][qb][4 * a4 + r] * inv);
+          for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][4 * a4 + r] * inv);
           *(u32x2*)(orow + d) = *(const u32x2*)o4;
         }
       }
   }
 }
 
-template <typename T, typename TO, int D, int QB>
+template <typename T, typename TO, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int BM = 128;
   const int ntq = (a.Nq + BM - 1) / BM;
   const int64_t grid = (int64_t)a.B * a.Hq * ntq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, TO, D, QB>), dim3((unsigned)grid), dim3(256), 0, s, a, ntq);
+  hipLaunchKernelGGL((prefill_kernel<T, TO, D>), dim3((unsigned)grid), dim3(256), 0, s, a, ntq);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s) {
-  constexpr int QB = 1;
   if (elem == 2) {
-    if (out_f32) return a.D == 64 ? launch_t<__bf16, float, 64, QB>(a, s) : launch_t<__bf16, float, 128, QB>(a, s);
-    return a.D == 64 ? launch_t<__bf16, __bf16, 64, QB>(a, s) : launch_t<__bf16, __bf16, 128, QB>(a, s);
+    if (out_f32) return a.D == 64 ? launch_t<__bf16, float, 64>(a, s) : launch_t<__bf16, float, 128>(a, s);
+    return a.D == 64 ? launch_t<__bf16, __bf16, 64>(a, s) : launch_t<__bf16, __bf16, 128>(a, s);
   }
-  return a.D == 64 ? launch_t<_Float16, _Float16, 64, QB>(a, s) : launch_t<_Float16, _Float16, 128, QB>(a, s);
+  return a.D == 64 ? launch_t<_Float16, _Float16, 64>(a, s) : launch_t<_Float16, _Float16, 128>(a, s);
 }
 
 // fp32 -> bf16, round to nearest even (the hardware conversion).
