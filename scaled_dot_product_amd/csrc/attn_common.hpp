@@ -36,8 +36,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-bit element traits: the 8-wide operand vector and the MFMA on it.
 template <typename T> struct Elem;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <> struct Elem<__bf16> {
   typedef bf16x8 vec8;
+  // acc + (sum of the 8 elements of v), as 4 packed dot products with 1
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+    return acc;
+  }
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -45,6 +56,13 @@ template <> struct Elem<__bf16> {
 };
 template <> struct Elem<_Float16> {
   typedef f16x8 vec8;
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(f16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+    return acc;
+  }
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
