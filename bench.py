@@ -186,7 +186,16 @@ def cpu_baseline(w, budget_s=12.0):
 def run_extra(part):
     from scaled_dot_product_amd.inputs import WORKLOADS
     extra = {}
-    if part == "quant":
+    if part == "copy":
+        import torch
+        n = 1 << 30
+        x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        ms = time_events(lambda: y.copy_(x), 5, 2)
+        extra["copy"] = {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+                         "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        log(f"copy: 1 GiB in {ms:.3f} ms")
+    elif part == "quant":
         wq = WORKLOADS["video_dit_quant_32760"]
         ms_q = bench_prefill(wq, 10, 2)
         ms_prep = bench_quant_prep(wq)
@@ -218,6 +227,23 @@ def run_extra(part):
     return extra
 
 
+def recorded_traffic(kernel_source: str, record: str):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by the same counters on a plain copy), as recorded in
+    profiles/; None unless the record was taken on the current kernel source."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", record)) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, kernel_source), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,8 +251,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "quant", "sdxl"],
-                    help="time one secondary workload only (for kernel profiles)")
+    ap.add_argument("--only", choices=["decode", "quant", "sdxl", "copy"],
+                    help="time one secondary workload only (for kernel profiles); "
+                         "'copy' runs a plain 1 GiB device copy, the reference for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -282,7 +310,9 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_kernel<bf16,bf16,128,1>",
+                     "traffic": recorded_traffic("scaled_dot_product_amd/csrc/attn_prefill.hip",
+                                                 "prefill_video_dit_traffic.json"),
+                     "kernel": "prefill_kernel<bf16,bf16,128,1>",
                      "per_launch": "21.979 TFLOP (4*B*H*N*N*D)"},
         "cpu_baseline": cpu,
         "extra": extra,
