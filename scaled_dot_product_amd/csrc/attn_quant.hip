@@ -4,8 +4,8 @@
 // section 1 of "Attention kernels on a home RTX 5080": Q and K become
 // symmetric INT8 codes with one fp32 scale per 64-token block of one head,
 // V becomes OCP FP8 E4M3 codes with one scale per 64-token block, and the
-// softmax weights are rounded to E4M3 at the static scale 448 (each weight is
-// at most 1 because the running maximum is always current in this kernel).
+// softmax weights are rounded to E4M3 with a static scale (each weight is at
+// most 1 because the running maximum is always current in this kernel).
 //
 //   quant_int8_kernel   per block: amax, scale = amax/127, inv = 127/amax,
 //                       code = clamp(rint(x*inv), -127, 127)  (bit-exact)
@@ -15,10 +15,12 @@
 //   prefill_quant_kernel
 //     S_int^T = Kc Qc^T              i8 MFMA 32x32x32, exact int32
 //     exponent = S_int * (s_q s_k scale log2 e) - m   (one FMA per score)
-//     P^ = E4M3(448 * 2^exponent), l += 448 * 2^exponent
-//     T^T = Vc^T P^T                 fp8 MFMA 32x32x64, fp32 accumulation
-//     O_acc = alpha O_acc + s_v T    (s_v: the tile's V block scale)
-//   O = O_acc / l.
+//     P^ = E4M3(448 P s_v / s_ref)   (s_v: the tile's V block scale, s_ref
+//                                     the head's largest; folded into the
+//                                     exponent's bias)
+//     O_acc += Vc^T P^T              fp8 MFMA 32x32x64, fp32 accumulation
+//     l += sum of P (unquantised)
+//   O = O_acc * s_ref / 448 / l.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
@@ -185,7 +187,18 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// Quantised prefill: 4 waves x 32 query rows, 64-key tiles.
+// Quantised prefill: 4 waves x 32 query rows, 64-key tiles, two workgroups
+// per CU, software-pipelined like the exact kernel (S of tile i+1 on the
+// matrix cores while the exponentials of tile i run; code tiles go straight
+// from HBM into XOR-swizzled LDS tiles).
+//
+// The V block scale s_v changes from tile to tile. Rather than rescale the
+// fp32 output by s_v after every tile, each tile's weights are quantised as
+// E4M3(448 P s_v / s_ref) with s_ref the largest V block scale of the head:
+// the factor 448 s_v / s_ref <= 448 goes into the exponent's bias (free),
+// the fp8 products accumulate straight into O, and the epilogue multiplies
+// by s_ref / 448 once. The denominator sums the unquantised weights (the
+// exponentials taken back by the same per-tile factor).
 template <typename TO, int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
@@ -193,17 +206,20 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
                      const float* __restrict__ ks, const uint8_t* __restrict__ vct,
                      const float* __restrict__ vs) {
   constexpr int BM = 128;
-  constexpr int KS = D / 32;      // i8 k-steps (32 channels each)
+  constexpr int KS = D / 32;       // i8 k-steps (32 channels each)
   constexpr int DB = D / 32;
-  constexpr int KLD = D + 16;     // K code tile row stride (bytes)
-  constexpr int VLD = 64 + 16;    // V^T code tile row stride (bytes)
-  constexpr int KCH = 64 * D / 16 / 256;   // 16-byte K chunks per thread
-  constexpr int VCH = D * 64 / 16 / 256;   // 16-byte V^T chunks per thread
-  constexpr float kP = 8.807354922057604f; // log2(448)
-  __shared__ __attribute__((aligned(16))) uint8_t sk[2][64 * KLD];
-  __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * VLD];
+  constexpr int KCPR = D / 16;     // 16-byte chunks per K code row
+  constexpr int KRPI = 64 / KCPR;  // K rows per direct-load instruction
+  constexpr float kLog2_448 = 8.807354922057604f;
+  // exp2 rounds within an ulp or so; lowering the bias by 2^-12 keeps every
+  // scaled weight <= 448 (the largest E4M3 magnitude) without a clamp
+  constexpr float kMargin = 2.44140625e-4f;
+  __shared__ __attribute__((aligned(16))) uint8_t sk[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * 64];
+  __shared__ float sred[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / ntq, qt = tile - bh * ntq;
@@ -223,11 +239,20 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   const int kv_lo = a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
   const int t_lo = kv_lo / 64;
-  const int t_hi = kv_hi > kv_lo ? (kv_hi + 63) / 64 : t_lo;
+  const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
+
+  // s_ref over the visible tiles (0 only when every one of those V blocks is 0).
+  float sref = 0.0f;
+  for (int t = t_lo + tid; t < t_lo + nt; t += 256) sref = fmaxf(sref, Vs[t]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sref = fmaxf(sref, __shfl_xor(sref, off, 64));
+  if (lane == 0) sred[wave] = sref;
+  __syncthreads();
+  sref = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
 
   const int qrow = q0 + wave * 32 + col;
   const int qw0 = q0 + wave * 32;
-  // Q codes as B operands: lane half h of k-step ks holds channels 32 ks + 16 h + (0..15).
+  // Q codes as B operands: lane half h of k-step k holds channels 32 k + 16 h + (0..15).
   i32x4 qv[KS];
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
@@ -236,40 +261,33 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     qv[k] = __builtin_bit_cast(i32x4, raw);
   }
   // The wave's 32 rows lie in one 64-row block (q0 is a multiple of 128).
-  const float sq = qs[(int64_t)bh * ((a.Nq + 63) / 64) + min(qw0, a.Nq - 1) / 64];
-  const float cq = sq * a.c;
+  const float cq = qs[(int64_t)bh * ((a.Nq + 63) / 64) + min(qw0, a.Nq - 1) / 64] * a.c;
 
-  u32x4 kreg[KCH], vreg[VCH];
-  auto gload = [&](int t) {
+  // K code row r holds key 32 h + 16 blk + 4 a + b for r = 32 blk + 8 a + 4 h + b,
+  // so lane half h's 32 scores of a tile are keys 32 h .. 32 h + 31 in B-operand
+  // slot order. Chunk c of a row sits at position c ^ kswz(r), chunk c of V^T row
+  // d (64 keys) at c ^ vswz(d): the 16 lanes of an operand read hit distinct banks.
+  auto kswz = [](int r) { return KCPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  auto vswz = [](int d) { return (d >> 2) & 3; };
+  auto load_k = [&](int t, int buf) {
+    const int8_t* base = Kc + (int64_t)64 * t * D;
+    const int last = a.Nk - 1 - 64 * t;   // rows past it clamp to the last key (masked)
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int kk = ch / (D / 16), c = ch - kk * (D / 16);
-      const int key = min(64 * t + kk, a.Nk - 1);   // clamped rows are masked
-      kreg[u] = ld16(Kc + (int64_t)key * D + 16 * c);
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int ch = tid + 256 * u;
-      vreg[u] = ld16(Vt + (int64_t)t * D * 64 + 16 * ch);
+    for (int u = 0; u < 16 / KRPI; ++u) {
+      const int r0 = 16 * wave + KRPI * u;
+      const int r = r0 + lane / KCPR, pos = lane % KCPR;
+      const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+      const uint32_t off = (uint32_t)(min(key, last) * D + 16 * (pos ^ kswz(r)));
+      load_to_lds16(base + off, &sk[buf][r0 * D]);
     }
   };
-  // K code row for key kk in the tile: C-row m = 8a + 4h + b of block blk holds
-  // key 32h + 16blk + 4a + b, so lane half h's 32 scores are keys 32h..32h+31.
-  auto lstore = [&](int buf) {
+  auto load_v = [&](int t, int buf) {
+    const uint8_t* base = Vt + (int64_t)t * D * 64;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int kk = ch / (D / 16), c = ch - kk * (D / 16);
-      const int hh = kk >> 5, blk = (kk >> 4) & 1, aa = (kk >> 2) & 3, bb = kk & 3;
-      const int row = 32 * blk + 8 * aa + 4 * hh + bb;
-      st16(&sk[buf][row * KLD + 16 * c], kreg[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int d = ch >> 2, j = ch & 3;
-      st16(&sv[buf][d * VLD + 16 * j], vreg[u]);
+    for (int u = 0; u < D / 64; ++u) {
+      const int d0 = (D / 4) * wave + 16 * u;
+      const int d = d0 + lane / 4, pos = lane % 4;
+      load_to_lds16(base + d * 64 + 16 * (pos ^ vswz(d)), &sv[buf][d0 * 64]);
     }
   };
 
@@ -280,38 +298,39 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (t_lo < t_hi) {
-    gload(t_lo);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const int k0 = 64 * t;
-    if (t + 1 < t_hi) gload(t + 1);
-
-    i32x16 s[2];
+  auto s_mma = [&](int buf, i32x16 (&s)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[mb][j] = 0;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const i32x4 ka = *(const i32x4*)&sk[buf][(32 * mb + col) * KLD + 32 * k + 16 * half];
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + col;
+        const i32x4 ka = *(const i32x4*)&sk[buf][r * D + 16 * ((2 * k + half) ^ kswz(r))];
         s[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv[k], s[mb], 0, 0, 0);
       }
-    }
+  };
+
+  auto step = [&](int i, i32x16 (&cur)[2], i32x16 (&nxt)[2]) {
+    const int t = t_lo + i;
+    if (i + 2 < nt) load_k(t + 2, i & 1);
+    if (i + 1 < nt) load_v(t + 1, (i + 1) & 1);
     // A block of zero codes has scale 0; a positive floor keeps masked scores
     // at -inf (-inf * 0 would be NaN) and changes nothing else, as every score
     // of such a block is exactly 0.
     const float cf = fmaxf(cq * Ks[t], 1.17549435e-38f);
+    const float sv_t = Vs[t];
+    const float ratio = sref > 0.0f ? fmaxf(sv_t / sref, 9.5367431640625e-7f) : 1.0f;
+    const float bias = __builtin_amdgcn_logf(ratio) + (kLog2_448 - kMargin);   // log2
     float sf[2][16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sf[mb][j] = (float)s[mb][j];
-    const bool need_mask = (k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0);
-    if (need_mask) {
+      for (int j = 0; j < 16; ++j) sf[mb][j] = (float)cur[mb][j];
+    const int k0 = 64 * t;
+    if ((k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -327,17 +346,24 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sf[1][j]);
     mx = halves_max(mx) * cf;
-    float alpha = 1.0f;
+    // the running maximum must be current: every scaled weight stays <= 448
     if (__builtin_amdgcn_ballot_w64(mx > m_run)) {
+      asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mx);
-      alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
       m_run = m_new;
     }
-    // 448 * P, one E4M3 code per score; the running max is current, so <= 448.
-    const float mu = (m_run == -INFINITY ? 0.0f : m_run) - kP;
+    const float mu = (m_run == -INFINITY ? 0.0f : m_run) - bias;
+
+    // S of tile i + 1 (i8 MFMA) interleaved with the weights of tile i.
+    s_mma((i + 1) & 1, nxt);
     i32x8 pb;
-    float lsum = 0.0f;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -346,37 +372,59 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -mu));
-          lsum += e[k];
-          e[k] = fminf(e[k], 448.0f);  // exp2 rounding may land a hair above 448
+          ls[k] += e[k];
         }
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
         pb[4 * mb + q4] = pk;
       }
-    l_run += lsum;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * KS - 2; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * KS), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    // back to unscaled weights for the denominator
+    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * __builtin_amdgcn_exp2f(-bias);
 
-    // T^T = Vc^T P^T (fp8 x fp8 -> fp32), then O_acc = alpha O_acc + s_v T.
-    const float sv_t = Vs[t];
+    // O^T += V^T P^T (fp8 x fp8 -> fp32) for tile i: one MFMA per 32 channels.
+    const int vb = i & 1;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const uint8_t* vp = &sv[buf][(32 * db + col) * VLD + 32 * half];
-      const u32x4 lo = ld16(vp), hi = ld16(vp + 16);
+      const int d = 32 * db + col;
+      const uint8_t* row = &sv[vb][d * 64];
+      const u32x4 lo = ld16(row + 16 * ((2 * half) ^ vswz(d)));
+      const u32x4 hi = ld16(row + 16 * ((2 * half + 1) ^ vswz(d)));
       const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      f32x16 tacc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) tacc[j] = 0.0f;
-      tacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, tacc, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][j] = fmaf(oacc[db][j], alpha, sv_t * tacc[j]);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, 127, 0, 127);
     }
-
-    if (t + 1 < t_hi) lstore(buf ^ 1);
+    vmem_wait_all();
     __syncthreads();
+  };
+
+  if (nt > 0) {
+    load_k(t_lo, 0);
+    load_v(t_lo, 0);
+    if (nt > 1) load_k(t_lo + 1, 1);
+    vmem_wait_all();
+    __syncthreads();
+    i32x16 s0[2], s1[2];
+    s_mma(0, s0);
+    __syncthreads();   // step 0 overwrites the K buffer just read
+    int i = 0;
+    for (; i + 1 < nt; i += 2) {
+      step(i, s0, s1);
+      step(i + 1, s1, s0);
+    }
+    if (i < nt) step(i, s0, s1);
   }
 
   const float l = halves_sum(l_run);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  // undo the fp8 weight scaling: 448 * 2^-margin / s_ref
+  const float inv = l > 0.0f ? (sref * __builtin_amdgcn_exp2f(kMargin) / 448.0f) / l : 0.0f;
   if (qrow < a.Nq) {
     TO* orow = Op + (int64_t)qrow * D;
 #pragma unroll

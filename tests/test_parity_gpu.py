@@ -200,26 +200,38 @@ def test_quant_mode_small(case):
     emu = oracle.attn_quant(q, k, v, scale=w.scale, causal=causal, window_lo=wlo, pos0=pos0)
     rel_emu, _ = metrics(out.double().numpy(), emu)
     print(f"    vs quantised emulation: {rel_emu:.4f} (vs exact {rel:.4f})")
-    # the GPU rounds P at the running maximum, the emulation at the final one:
-    # both are quantisations of the same weights, so they agree far better
-    # than either agrees with exact attention.
+    # the GPU rounds P at the running maximum and per key block at a scale
+    # that carries V's block scale, the emulation at the final maximum and a
+    # static scale: both are quantisations of the same weights, so they agree
+    # far better than either agrees with exact attention.
     assert rel_emu <= rel
     for i in masked_rows(w):
         assert torch.all(out[:, :, i] == 0), i
 
 
-def test_quant_mode_zero_q_is_mean_of_vhat():
-    # Q = 0: scores all 0, weights uniform and exactly representable -> mean of V^
+def test_quant_mode_zero_q_closed_form():
+    # Q = 0: every score is 0 and every weight 1. Key block t's weights are
+    # rounded once, to E4M3(448 s_v,t / s_ref) / (448 s_v,t / s_ref) with s_ref
+    # the largest V block scale the query tile sees, so the output is the
+    # block-weighted mean of V^ with those factors (plain mean where s_v,t = s_ref).
     w = Workload("qzero", 1, 2, 2, 64, 300, 128, torch.bfloat16, mode=1)
     _, k, v = make_qkv(w)
     q = torch.zeros(w.q_shape, dtype=torch.bfloat16)
     out = gpu_fwd(w, q, k, v).double().cpu().numpy()
     vc, vs = oracle.quant_e4m3(v)
     dec = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    gap = 0.0
     for h in range(2):
-        vhat = dec[vc[0, h]] * np.repeat(vs[0, h].astype(np.float64), 64)[:300, None]
-        want = vhat.mean(axis=0)
-        np.testing.assert_allclose(out[0, h], np.broadcast_to(want, (64, 128)), rtol=0, atol=1e-2)
+        s_v = vs[0, h].astype(np.float64)
+        vhat = dec[vc[0, h]] * np.repeat(s_v, 64)[:300, None]
+        ratio = s_v / s_v.max()
+        wt = np.array([oracle.e4m3_decode(oracle.e4m3_encode(np.float32(448.0 * r))) / (448.0 * r)
+                       for r in ratio])
+        want = (np.repeat(wt, 64)[:300, None] * vhat).sum(axis=0) / 300.0
+        np.testing.assert_allclose(out[0, h], np.broadcast_to(want, (64, 128)), rtol=0, atol=1e-3)
+        gap = max(gap, np.abs(want - vhat.mean(axis=0)).max())
+    # the per-block factors are not all 1 here, so this also checks they are applied
+    assert gap > 3e-3
 
 
 # ---- fused decode: workspace state and graph replay --------------------------
