@@ -100,13 +100,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
 #endif
 }
 
-// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_base + 16 i (lds_base must be the same for the whole wave).
-__device__ __forceinline__ void load_to_lds16(const void* g, void* lds_base) {
+// Direct global -> LDS load of 16 bytes per lane: lane i's 16 bytes, read
+// from base + off_i, land at lds_base + 16 i (base and lds_base must be the
+// same for the whole wave; M0 carries the LDS address). Written as inline asm
+// so that the compiler does not order later LDS reads of other tiles behind
+// it: it would otherwise make every LDS read wait for all direct loads still
+// in flight. The caller makes the tile visible with vmem_wait_all() and a
+// workgroup barrier before any wave reads it.
+__device__ __forceinline__ void load_to_lds16(const void* base, uint32_t off, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0) : "memory");
 #else
-  (void)g;
+  (void)base;
+  (void)off;
   (void)lds_base;
 #endif
 }

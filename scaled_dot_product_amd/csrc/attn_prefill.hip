@@ -15,23 +15,21 @@
 // before the epilogue divides by the running sum. The N x N score matrix is
 // never stored.
 //
-// The loop is software-pipelined so the matrix cores do not wait for the
-// softmax: iteration i computes S for tile i+1 on the MFMA pipe while the
-// vector ALU exponentiates tile i, then accumulates P V for tile i. K tile
-// i+1 and V tile i are resident together, so K and V use separate LDS double
-// buffers offset by one tile, and one barrier per iteration suffices. The
-// instruction interleave inside an iteration is fixed with scheduling-group
-// barriers.
+// The loop is software-pipelined so that both halves of the work always have
+// matrix-core instructions beside them: iteration i first accumulates P V of
+// tile i-1 on the MFMA pipe while the vector ALU takes the row maxima of tile
+// i, then computes S of tile i+1 while the vector ALU exponentiates tile i.
+// K tiles are loaded two iterations ahead, V tiles one; K and V use separate
+// LDS double buffers and one barrier per iteration suffices. The instruction
+// interleave inside each half is fixed with scheduling-group barriers.
 //
 // 64-key tiles follow the 64-position KV chunk of "perf(metal): widen
 // four-row flash KV tiles" (its 128-position chunk is a different trade-off,
 // for a four-row shape on another GPU).
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
-
-#ifndef PREFILL_QB128
-#define PREFILL_QB128 1
-#endif
 
 namespace attn {
 
@@ -48,13 +46,23 @@ constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <typename T, typename TO, int D, int QB>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+// LDS operand reads issued ahead of the MFMA that consumes them (K reads in
+// the S half, V transpose-read pairs in the P V half).
+#ifndef PREFILL_KPRE
+#define PREFILL_KPRE 4
+#endif
+#ifndef PREFILL_VPRE
+#define PREFILL_VPRE 4
+#endif
+constexpr int kKPre = PREFILL_KPRE;
+constexpr int kVPre = PREFILL_VPRE;
+
+template <typename T, typename TO, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(FwdArgs a, int ntq) {
   using E = Elem<T>;
   using V8 = typename E::vec8;
-  constexpr int BM = 128 * QB;
+  constexpr int BM = 128;
   constexpr int KS = D / 16;       // 16-wide k-steps of Q K^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
@@ -84,20 +92,15 @@ prefill_kernel(FwdArgs a, int ntq) {
   const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
 
   // Q^T as B operands, held for the whole loop: column = query row,
-  // lane half h of k-step ks holds d = 16 ks + 8 h + (0..7). A wave owns
-  // QB blocks of 32 rows.
-  const int qw0 = q0 + wave * 32 * QB;  // first row of this wave
-  int qrow[QB];
-  V8 qv[QB][KS];
+  // lane half h of k-step ks holds d = 16 ks + 8 h + (0..7).
+  const int qw0 = q0 + wave * 32;   // first row of this wave
+  const int qrow = qw0 + col;
+  V8 qv[KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = qw0 + 32 * qb + col;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 raw = {0, 0, 0, 0};
-      if (qrow[qb] < a.Nq) raw = ld16(Qp + (int64_t)qrow[qb] * D + 16 * ks + 8 * half);
-      qv[qb][ks] = __builtin_bit_cast(V8, raw);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 raw = {0, 0, 0, 0};
+    if (qrow < a.Nq) raw = ld16(Qp + (int64_t)qrow * D + 16 * ks + 8 * half);
+    qv[ks] = __builtin_bit_cast(V8, raw);
   }
 
   // LDS tiles are 64 unpadded rows of D elements; chunk c of row r sits at
@@ -121,7 +124,7 @@ prefill_kernel(FwdArgs a, int ntq) {
       const int r = r0 + lane / CPR, pos = lane % CPR;
       const int kk = (r & ~31) | swap23(r & 31);
       const uint32_t off = (uint32_t)(min(kk, last) * (D * 2) + 16 * (pos ^ kswz(r)));
-      load_to_lds16(base + off, &sk[buf][r0 * D]);
+      load_to_lds16(base, off, &sk[buf][r0 * D]);
     }
   };
   auto load_v = [&](int t, int buf) {
@@ -132,143 +135,57 @@ prefill_kernel(FwdArgs a, int ntq) {
       const int r0 = 16 * wave + RPI * u;
       const int r = r0 + lane / CPR, pos = lane % CPR;
       const uint32_t off = (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r)));
-      load_to_lds16(base + off, &sv[buf][r0 * D]);
+      load_to_lds16(base, off, &sv[buf][r0 * D]);
     }
   };
 
   // Boundary tiles only: window edge, ragged end, causal diagonal.
-  auto apply_mask = [&](f32x16 (&s)[2][QB], int t) {
+  auto apply_mask = [&](f32x16 (&s)[2], int t) {
     const int k0 = 64 * t;
     const bool need = (k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0);
     if (need) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-            const bool vis = key >= kv_lo && key < a.Nk && (!a.causal || key <= a.pos0 + qrow[qb]);
-            if (!vis) s[mb][qb][j] = -INFINITY;
-          }
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
+          const bool vis = key >= kv_lo && key < a.Nk && (!a.causal || key <= a.pos0 + qrow);
+          if (!vis) s[mb][j] = -INFINITY;
+        }
     }
   };
 
-  f32x16 oacc[DB][QB];
+  f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][qb][j] = 0.0f;
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
-  }
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  // P^T of the previous tile, waiting for its P V product.
+  V8 pprev[2][2];
 
-  // S^T of one tile from an LDS K buffer (2 * QB independent MFMA chains;
-  // every K operand read feeds QB MFMAs).
-  auto s_mma = [&](int buf, f32x16 (&s)[2][QB]) {
+  // S^T of one tile from an LDS K buffer (two independent MFMA chains).
+  auto s_mma = [&](int buf, f32x16 (&s)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s[mb][qb][j] = 0.0f;
+      for (int j = 0; j < 16; ++j) s[mb][j] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int r = 32 * mb + col;
         const V8 ka = *(const V8*)&sk[buf][r * D + 8 * ((2 * ks + half) ^ kswz(r))];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[mb][qb] = E::mma(ka, qv[qb][ks], s[mb][qb]);
+        s[mb] = E::mma(ka, qv[ks], s[mb]);
       }
   };
 
-  // One pipeline step: softmax and P V of tile i (scores in cur), S of tile
-  // i + 1 into nxt, then the stores and loads that keep K two tiles and V one
-  // tile ahead.
-  auto step = [&](int i, f32x16 (&cur)[2][QB], f32x16 (&nxt)[2][QB]) {
-    const int t = t_lo + i;
-    // K tile i + 2 goes where K tile i was, V tile i + 1 where V tile i - 1
-    // was (both last read before the previous barrier); they land during
-    // this step and are published by its closing barrier.
-    if (i + 2 < nt) load_k(t + 2, i & 1);
-    if (i + 1 < nt) load_v(t + 1, (i + 1) & 1);
-    apply_mask(cur, t);
-    float mu[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = cur[0][qb][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, cur[0][qb][j]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][qb][j]);
-      mx = halves_max(mx) * a.c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazyLog2)) {
-        // rare after the first tiles; the empty asm keeps this a real branch
-        // (the compiler would otherwise run the rescale on every tile)
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[db][qb][j] *= alpha;
-        m_run[qb] = m_new;
-      }
-      mu[qb] = m_run[qb] == -INFINITY ? 0.0f : m_run[qb];
-    }
-
-    // S of tile i + 1 (MFMA) interleaved with the exponentials of tile i.
-    __builtin_amdgcn_s_setprio(1);
-    s_mma((i + 1) & 1, nxt);
-    V8 pv[QB][2][2];
-    float ls[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ls[qb][k] = 0.0f;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          V8 p;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            p[q] = E::from_float(__builtin_amdgcn_exp2f(fmaf(cur[mb][qb][8 * tt + q], a.c, -mu[qb])));
-          pv[qb][mb][tt] = p;
-          // the denominator sums the rounded weights the P V product uses
-          ls[qb][2 * mb + tt] = E::sum8(p, ls[qb][2 * mb + tt]);
-        }
-    // 2*KS*QB MFMAs with the exponentials spread between them; the K reads
-    // run ahead of the MFMAs that use them.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * KS - 2; ++k) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / KS, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * QB, 0);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += (ls[qb][0] + ls[qb][1]) + (ls[qb][2] + ls[qb][3]);
-
-    // O^T += V^T P^T for tile i (4 k-steps of 16 keys, DB * QB chains). In
-    // each 16-lane group the transpose read hands lane 4a + e element e of
-    // the rows named by lanes a, a+4, a+8, a+12: lane r names key kb + r/4
-    // at channel d0 + 4 (r % 4), so lane (col, half) gets channel col of keys
-    // kb..kb+3, i.e. four B-operand slots of P^T's order.
-    const int vb = i & 1;
+  // O^T += V^T P^T for one tile (4 k-steps of 16 keys, DB chains). In each
+  // 16-lane group the transpose read hands lane 4a + e element e of the rows
+  // named by lanes a, a+4, a+8, a+12: lane r names key kb + r/4 at channel
+  // d0 + 4 (r % 4), so lane (col, half) gets channel col of keys kb..kb+3,
+  // i.e. four B-operand slots of P^T's order.
+  auto pv_mma = [&](int vb) {
     const int gq = lane >> 4, rr = lane & 15;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -287,40 +204,127 @@ prefill_kernel(FwdArgs a, int ntq) {
           const s16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
                               part[1][0], part[1][1], part[1][2], part[1][3]};
           const V8 va = __builtin_bit_cast(V8, both);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = E::mma(va, pv[qb][mb][tt], oacc[db][qb]);
+          oacc[db] = E::mma(va, pprev[mb][tt], oacc[db]);
         }
+  };
 
-    __builtin_amdgcn_s_setprio(0);
+  // One pipeline step for tile i (scores in cur): P V of tile i - 1 beside
+  // the row maxima of tile i, then S of tile i + 1 into nxt beside the
+  // exponentials of tile i.
+  auto step = [&](auto first, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr bool kFirst = decltype(first)::value;
+    const int t = t_lo + i;
+    // K tile i + 2 goes where K tile i was (read before the previous
+    // barrier), V tile i where V tile i - 2 was (its P V ran in the previous
+    // step); both land during this step and are published by its closing
+    // barrier.
+    if (i + 2 < nt) load_k(t + 2, i & 1);
+    load_v(t, i & 1);
+    apply_mask(cur, t);
+
+    if constexpr (!kFirst) pv_mma((i - 1) & 1);
+    float mx = cur[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, cur[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][j]);
+    mx = halves_max(mx) * a.c;
+    if constexpr (!kFirst) {
+      // 4 DB MFMAs with the maxima spread between them; transpose reads
+      // run ahead of the MFMAs that use them.
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPre, 0);
+#pragma unroll
+      for (int k = 0; k < 4 * DB; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+        if (k < 4 * DB - kVPre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
+      // rare after the first tiles; the empty asm keeps this a real branch
+      // (the compiler would otherwise run the rescale on every tile). O
+      // already holds tile i - 1 here.
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m_run = m_new;
+    }
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
+
+    // S of tile i + 1 (MFMA) interleaved with the exponentials of tile i.
+    s_mma((i + 1) & 1, nxt);
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        V8 p;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          p[q] = E::from_float(__builtin_amdgcn_exp2f(fmaf(cur[mb][8 * tt + q], a.c, -mu)));
+        pprev[mb][tt] = p;
+        // the denominator sums the rounded weights the P V product uses
+        ls[2 * mb + tt] = E::sum8(p, ls[2 * mb + tt]);
+      }
+    // 2*KS MFMAs with the exponentials spread between them; the K reads
+    // run ahead of the MFMAs that use them.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKPre, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * KS - kKPre; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / KS, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKPre, 0);
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // Pin the weights here: left alone, the compiler sinks the exponentials
+    // past the barrier to their first use in the next step, where the P V
+    // MFMAs would wait on them and no MFMA would run beside them.
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 w = __builtin_bit_cast(u32x4, pprev[mb][tt]);
+        asm volatile("" : "+v"(w));
+        pprev[mb][tt] = __builtin_bit_cast(V8, w);
+      }
+
     vmem_wait_all();   // this wave's direct-to-LDS loads have landed
     __syncthreads();
   };
 
   if (nt > 0) {
-    // Prologue: K tiles 0 and 1 and V tile 0 in LDS, S of tile 0.
+    // Prologue: K tiles 0 and 1 in LDS, S of tile 0.
     load_k(t_lo, 0);
-    load_v(t_lo, 0);
     if (nt > 1) load_k(t_lo + 1, 1);
     vmem_wait_all();
     __syncthreads();
-    f32x16 s0[2][QB], s1[2][QB];
+    f32x16 s0[2], s1[2];
     s_mma(0, s0);
     __syncthreads();   // step 0 overwrites the K buffer just read
-    int i = 0;
+    using First = std::true_type;
+    using Later = std::false_type;
+    step(First{}, 0, s0, s1);
+    int i = 1;
     for (; i + 1 < nt; i += 2) {
-      step(i, s0, s1);
-      step(i + 1, s1, s0);
+      step(Later{}, i, s1, s0);
+      step(Later{}, i + 1, s0, s1);
     }
-    if (i < nt) step(i, s0, s1);
+    if (i < nt) step(Later{}, i, s1, s0);
+    // P V of the last tile (its V tile was published by the last barrier).
+    pv_mma((nt - 1) & 1);
   }
 
   // Epilogue: O = O_acc / l; rows with no visible key are written as zeros.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = halves_sum(l_run[qb]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (qrow[qb] >= a.Nq) continue;
-    TO* orow = Op + (int64_t)qrow[qb] * D;
+  const float l = halves_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qrow < a.Nq) {
+    TO* orow = Op + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -329,39 +333,36 @@ prefill_kernel(FwdArgs a, int ntq) {
         if constexpr (sizeof(TO) == 4) {
           f32x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][qb][4 * a4 + r] * inv;
+          for (int r = 0; r < 4; ++r) o4[r] = oacc[db][4 * a4 + r] * inv;
           *(f32x4*)(orow + d) = o4;
         } else {
           TO o4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][qb][4 * a4 + r] * inv);
+          for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][4 * a4 + r] * inv);
           *(u32x2*)(orow + d) = *(const u32x2*)o4;
         }
       }
   }
 }
 
-template <typename T, typename TO, int D, int QB>
+template <typename T, typename TO, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = 128 * QB;
+  constexpr int BM = 128;
   const int ntq = (a.Nq + BM - 1) / BM;
   const int64_t grid = (int64_t)a.B * a.Hq * ntq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, TO, D, QB>), dim3((unsigned)grid), dim3(256), 0, s, a, ntq);
+  hipLaunchKernelGGL((prefill_kernel<T, TO, D>), dim3((unsigned)grid), dim3(256), 0, s, a, ntq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Rows per wave: 64 for head dim 128 (one wave per SIMD, 512 registers),
-// 32 for head dim 64 (two waves per SIMD).
 hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s) {
-  constexpr int QB128 = PREFILL_QB128;
   if (elem == 2) {
-    if (out_f32) return a.D == 64 ? launch_t<__bf16, float, 64, 1>(a, s) : launch_t<__bf16, float, 128, QB128>(a, s);
-    return a.D == 64 ? launch_t<__bf16, __bf16, 64, 1>(a, s) : launch_t<__bf16, __bf16, 128, QB128>(a, s);
+    if (out_f32) return a.D == 64 ? launch_t<__bf16, float, 64>(a, s) : launch_t<__bf16, float, 128>(a, s);
+    return a.D == 64 ? launch_t<__bf16, __bf16, 64>(a, s) : launch_t<__bf16, __bf16, 128>(a, s);
   }
-  return a.D == 64 ? launch_t<_Float16, _Float16, 64, 1>(a, s) : launch_t<_Float16, _Float16, 128, QB128>(a, s);
+  return a.D == 64 ? launch_t<_Float16, _Float16, 64>(a, s) : launch_t<_Float16, _Float16, 128>(a, s);
 }
 
 // fp32 -> bf16, round to nearest even (the hardware conversion).

@@ -278,7 +278,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
       const int r = r0 + lane / KCPR, pos = lane % KCPR;
       const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
       const uint32_t off = (uint32_t)(min(key, last) * D + 16 * (pos ^ kswz(r)));
-      load_to_lds16(base + off, &sk[buf][r0 * D]);
+      load_to_lds16(base, off, &sk[buf][r0 * D]);
     }
   };
   auto load_v = [&](int t, int buf) {
@@ -287,7 +287,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     for (int u = 0; u < D / 64; ++u) {
       const int d0 = (D / 4) * wave + 16 * u;
       const int d = d0 + lane / 4, pos = lane % 4;
-      load_to_lds16(base + d * 64 + 16 * (pos ^ vswz(d)), &sv[buf][d0 * 64]);
+      load_to_lds16(base, (uint32_t)(d * 64 + 16 * (pos ^ vswz(d))), &sv[buf][d0 * 64]);
     }
   };
 
