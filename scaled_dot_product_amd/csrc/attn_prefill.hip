@@ -112,30 +112,49 @@ prefill_kernel(FwdArgs a, int ntq) {
   auto vswz = [](int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
   // Direct loads: each wave fills 16 rows of the K and of the V tile, RPI
   // rows per instruction (lane i -> row i / CPR, chunk position i % CPR).
-  // Rows past Nk are clamped to the last row (finite values; masked).
-  // Per-lane parts of the direct loads are loop invariant; the tile enters
-  // as a uniform base pointer and a clamp on the row.
+  // The per-lane byte offsets inside a tile are loop invariant; the tile
+  // enters as a uniform base pointer. In the ragged last tile, rows past Nk
+  // are clamped to the last row (finite values; masked).
+  constexpr int NL = 16 / RPI;   // direct loads per wave and tile
+  uint32_t kofs[NL], vofs[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int r = 16 * wave + RPI * u + lane / CPR, pos = lane % CPR;
+    const int kk = (r & ~31) | swap23(r & 31);
+    kofs[u] = (uint32_t)(kk * (D * 2) + 16 * (pos ^ kswz(r)));
+    vofs[u] = (uint32_t)(r * (D * 2) + 16 * (pos ^ vswz(r)));
+  }
   auto load_k = [&](int t, int buf) {
     const char* base = (const char*)(Kp + (int64_t)64 * t * D);
     const int last = a.Nk - 1 - 64 * t;   // rows past it clamp to the last key
+    if (last >= 63) {
 #pragma unroll
-    for (int u = 0; u < 16 / RPI; ++u) {
-      const int r0 = 16 * wave + RPI * u;
-      const int r = r0 + lane / CPR, pos = lane % CPR;
-      const int kk = (r & ~31) | swap23(r & 31);
-      const uint32_t off = (uint32_t)(min(kk, last) * (D * 2) + 16 * (pos ^ kswz(r)));
-      load_to_lds16(base, off, &sk[buf][r0 * D]);
+      for (int u = 0; u < NL; ++u) load_to_lds16(base, kofs[u], &sk[buf][(16 * wave + RPI * u) * D]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int r0 = 16 * wave + RPI * u;
+        const int r = r0 + lane / CPR, pos = lane % CPR;
+        const int kk = (r & ~31) | swap23(r & 31);
+        const uint32_t off = (uint32_t)(min(kk, last) * (D * 2) + 16 * (pos ^ kswz(r)));
+        load_to_lds16(base, off, &sk[buf][r0 * D]);
+      }
     }
   };
   auto load_v = [&](int t, int buf) {
     const char* base = (const char*)(Vp + (int64_t)64 * t * D);
     const int last = a.Nk - 1 - 64 * t;
+    if (last >= 63) {
 #pragma unroll
-    for (int u = 0; u < 16 / RPI; ++u) {
-      const int r0 = 16 * wave + RPI * u;
-      const int r = r0 + lane / CPR, pos = lane % CPR;
-      const uint32_t off = (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r)));
-      load_to_lds16(base, off, &sv[buf][r0 * D]);
+      for (int u = 0; u < NL; ++u) load_to_lds16(base, vofs[u], &sv[buf][(16 * wave + RPI * u) * D]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int r0 = 16 * wave + RPI * u;
+        const int r = r0 + lane / CPR, pos = lane % CPR;
+        const uint32_t off = (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r)));
+        load_to_lds16(base, off, &sv[buf][r0 * D]);
+      }
     }
   };
 

@@ -269,26 +269,42 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   // d (64 keys) at c ^ vswz(d): the 16 lanes of an operand read hit distinct banks.
   auto kswz = [](int r) { return KCPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
   auto vswz = [](int d) { return (d >> 2) & 3; };
+  // Per-lane byte offsets inside a tile are loop invariant; in the ragged last
+  // K tile, rows past Nk clamp to the last key (masked).
+  constexpr int NK = 16 / KRPI, NV = D / 64;
+  uint32_t kofs[NK], vofs[NV];
+#pragma unroll
+  for (int u = 0; u < NK; ++u) {
+    const int r = 16 * wave + KRPI * u + lane / KCPR, pos = lane % KCPR;
+    const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+    kofs[u] = (uint32_t)(key * D + 16 * (pos ^ kswz(r)));
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int d = (D / 4) * wave + 16 * u + lane / 4, pos = lane % 4;
+    vofs[u] = (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
+  }
   auto load_k = [&](int t, int buf) {
     const int8_t* base = Kc + (int64_t)64 * t * D;
-    const int last = a.Nk - 1 - 64 * t;   // rows past it clamp to the last key (masked)
+    const int last = a.Nk - 1 - 64 * t;
+    if (last >= 63) {
 #pragma unroll
-    for (int u = 0; u < 16 / KRPI; ++u) {
-      const int r0 = 16 * wave + KRPI * u;
-      const int r = r0 + lane / KCPR, pos = lane % KCPR;
-      const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
-      const uint32_t off = (uint32_t)(min(key, last) * D + 16 * (pos ^ kswz(r)));
-      load_to_lds16(base, off, &sk[buf][r0 * D]);
+      for (int u = 0; u < NK; ++u) load_to_lds16(base, kofs[u], &sk[buf][(16 * wave + KRPI * u) * D]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int r0 = 16 * wave + KRPI * u;
+        const int r = r0 + lane / KCPR, pos = lane % KCPR;
+        const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+        const uint32_t off = (uint32_t)(min(key, last) * D + 16 * (pos ^ kswz(r)));
+        load_to_lds16(base, off, &sk[buf][r0 * D]);
+      }
     }
   };
   auto load_v = [&](int t, int buf) {
     const uint8_t* base = Vt + (int64_t)t * D * 64;
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) {
-      const int d0 = (D / 4) * wave + 16 * u;
-      const int d = d0 + lane / 4, pos = lane % 4;
-      load_to_lds16(base, (uint32_t)(d * 64 + 16 * (pos ^ vswz(d))), &sv[buf][d0 * 64]);
-    }
+    for (int u = 0; u < NV; ++u) load_to_lds16(base, vofs[u], &sv[buf][((D / 4) * wave + 16 * u) * 64]);
   };
 
   f32x16 oacc[DB];
