@@ -227,19 +227,22 @@ def run_extra(part):
     return extra
 
 
-def recorded_traffic(kernel_source: str, record: str):
+def recorded_traffic(record: str):
     """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by the same counters on a plain copy), as recorded in
-    profiles/; None unless the record was taken on the current kernel source."""
+    profiles/; None unless the record was taken on the current kernel sources
+    (the SHA-256 of the listed source files, concatenated in order)."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", record)) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, kernel_source), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, ValueError):
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != h.hexdigest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -310,9 +313,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic("scaled_dot_product_amd/csrc/attn_prefill.hip",
-                                                 "prefill_video_dit_traffic.json"),
-                     "kernel": "prefill_kernel<bf16,bf16,128,1>",
+                     "traffic": recorded_traffic("prefill_video_dit_traffic.json"),
+                     "kernel": "prefill_kernel<bf16,bf16,128>",
                      "per_launch": "21.979 TFLOP (4*B*H*N*N*D)"},
         "cpu_baseline": cpu,
         "extra": extra,
