@@ -123,7 +123,7 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  if (tid == 0) claim_counter(p.ctr + bg, p.gen);
+  bool claimed = false;   // uniform: the counter is claimed after the first loads
 
   // This workgroup's tiles: [t0, t1); wave w takes t0 + w, t0 + w + kWaves, ...
   const int t0 = p.t_lo + split * p.tiles_per_wg;
@@ -151,6 +151,9 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
           const int key = min(k0 + 4 * kg + r, a.Nk - 1);
           vreg[u][r] = ld16(Vp + (int64_t)key * D + 8 * (c0 + 4 * u));
         }
+      // claim while this wave's tile loads are in flight (its wait on the
+      // counter read then overlaps the wait on the tile)
+      if (!claimed && tid == 0) claim_counter(p.ctr + bg, p.gen);
       // V^T into this wave's slab.
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
@@ -229,7 +232,10 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
       }
     }
     __syncthreads();
+    claimed = true;
   }
+  // A workgroup without tiles still claims before it arrives.
+  if (!claimed && tid == 0) claim_counter(p.ctr + bg, p.gen);
 
   // 1. Publish this workgroup's partial.
   const int64_t pbase = ((int64_t)bg * p.nsplit + split) * p.rows;
