@@ -57,12 +57,12 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int kKPre = PREFILL_KPRE;
 constexpr int kVPre = PREFILL_VPRE;
 
-template <typename T, typename TO, int D>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <typename T, typename TO, int D, int W>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(FwdArgs a, int ntq) {
   using E = Elem<T>;
   using V8 = typename E::vec8;
-  constexpr int BM = 128;
+  constexpr int BM = 32 * W;       // W waves of 32 query rows
   constexpr int KS = D / 16;       // 16-wide k-steps of Q K^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
@@ -110,50 +110,62 @@ prefill_kernel(FwdArgs a, int ntq) {
   // lanes of a V transpose read (4 rows x 8 chunks) hit distinct banks.
   auto kswz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz = [](int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
-  // Direct loads: each wave fills 16 rows of the K and of the V tile, RPI
-  // rows per instruction (lane i -> row i / CPR, chunk position i % CPR).
-  // The per-lane byte offsets inside a tile are loop invariant; the tile
-  // enters as a uniform base pointer. In the ragged last tile, rows past Nk
-  // are clamped to the last row (finite values; masked).
-  constexpr int NL = 16 / RPI;   // direct loads per wave and tile
+  // Direct loads: a tile takes NLK instructions of RPI rows each for K and as
+  // many for V (lane i -> row i / CPR, chunk position i % CPR). With at least
+  // W of them, wave w loads NL consecutive instructions of each tile; with
+  // fewer (head dim 64, 8 waves), waves 0 .. NLK-1 load K and the last NLK
+  // waves load V, one instruction each. The per-lane byte offsets inside a
+  // tile are loop invariant; the tile enters as a uniform base pointer. In
+  // the ragged last tile, rows past Nk are clamped to the last row (finite
+  // values; masked).
+  constexpr int NLK = 64 / RPI;
+  constexpr bool kSplitKV = NLK < W;
+  constexpr int NL = kSplitKV ? 1 : NLK / W;   // K (and V) instructions per wave
+  static_assert(kSplitKV ? 2 * NLK == W : NL * W == NLK, "direct loads must split evenly");
+  const bool loads_k = !kSplitKV || wave < NLK;
+  const bool loads_v = !kSplitKV || wave >= W - NLK;
+  const int kr0 = kSplitKV ? RPI * wave : RPI * NL * wave;             // first K row
+  const int vr0 = kSplitKV ? RPI * (wave - (W - NLK)) : RPI * NL * wave;  // first V row
+  auto krow = [](int r) { return (r & ~31) | swap23(r & 31); };   // key held by K row r
   uint32_t kofs[NL], vofs[NL];
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
-    const int r = 16 * wave + RPI * u + lane / CPR, pos = lane % CPR;
-    const int kk = (r & ~31) | swap23(r & 31);
-    kofs[u] = (uint32_t)(kk * (D * 2) + 16 * (pos ^ kswz(r)));
-    vofs[u] = (uint32_t)(r * (D * 2) + 16 * (pos ^ vswz(r)));
+    const int pos = lane % CPR;
+    const int rk = kr0 + RPI * u + lane / CPR, rv = vr0 + RPI * u + lane / CPR;
+    kofs[u] = (uint32_t)(krow(rk) * (D * 2) + 16 * (pos ^ kswz(rk)));
+    vofs[u] = (uint32_t)(rv * (D * 2) + 16 * (pos ^ vswz(rv)));
   }
   auto load_k = [&](int t, int buf) {
+    if (!loads_k) return;
     const char* base = (const char*)(Kp + (int64_t)64 * t * D);
     const int last = a.Nk - 1 - 64 * t;   // rows past it clamp to the last key
     if (last >= 63) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u) load_to_lds16(base, kofs[u], &sk[buf][(16 * wave + RPI * u) * D]);
+      for (int u = 0; u < NL; ++u) load_to_lds16(base, kofs[u], &sk[buf][(kr0 + RPI * u) * D]);
     } else {
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const int r0 = 16 * wave + RPI * u;
+        const int r0 = kr0 + RPI * u;
         const int r = r0 + lane / CPR, pos = lane % CPR;
-        const int kk = (r & ~31) | swap23(r & 31);
-        const uint32_t off = (uint32_t)(min(kk, last) * (D * 2) + 16 * (pos ^ kswz(r)));
-        load_to_lds16(base, off, &sk[buf][r0 * D]);
+        load_to_lds16(base, (uint32_t)(min(krow(r), last) * (D * 2) + 16 * (pos ^ kswz(r))),
+                      &sk[buf][r0 * D]);
       }
     }
   };
   auto load_v = [&](int t, int buf) {
+    if (!loads_v) return;
     const char* base = (const char*)(Vp + (int64_t)64 * t * D);
     const int last = a.Nk - 1 - 64 * t;
     if (last >= 63) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u) load_to_lds16(base, vofs[u], &sv[buf][(16 * wave + RPI * u) * D]);
+      for (int u = 0; u < NL; ++u) load_to_lds16(base, vofs[u], &sv[buf][(vr0 + RPI * u) * D]);
     } else {
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const int r0 = 16 * wave + RPI * u;
+        const int r0 = vr0 + RPI * u;
         const int r = r0 + lane / CPR, pos = lane % CPR;
-        const uint32_t off = (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r)));
-        load_to_lds16(base, off, &sv[buf][r0 * D]);
+        load_to_lds16(base, (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r))),
+                      &sv[buf][r0 * D]);
       }
     }
   };
@@ -364,14 +376,25 @@ prefill_kernel(FwdArgs a, int ntq) {
   }
 }
 
-template <typename T, typename TO, int D>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = 128;
+template <typename T, typename TO, int D, int W>
+hipError_t launch_w(const FwdArgs& a, hipStream_t s) {
+  constexpr int BM = 32 * W;
   const int ntq = (a.Nq + BM - 1) / BM;
   const int64_t grid = (int64_t)a.B * a.Hq * ntq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, TO, D>), dim3((unsigned)grid), dim3(256), 0, s, a, ntq);
+  hipLaunchKernelGGL((prefill_kernel<T, TO, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a, ntq);
   return hipGetLastError();
+}
+
+// Eight waves (256 query rows) per workgroup halve the direct-load traffic
+// into LDS per flop, but one such workgroup fills a CU, so the last round of
+// workgroups runs the machine partly idle: they are used only for head dim
+// 128 when the grid is at least eight rounds of 256 workgroups.
+template <typename T, typename TO, int D>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+  const int64_t grid8 = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256);
+  if (D == 128 && grid8 >= 8 * 256) return launch_w<T, TO, D, 8>(a, s);
+  return launch_w<T, TO, D, 4>(a, s);
 }
 
 }  // namespace

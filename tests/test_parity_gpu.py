@@ -77,6 +77,28 @@ def test_prefill_edges(case):
         assert torch.all(out[:, :, i] == 0), i
 
 
+# Grids of at least eight rounds of 256-row workgroups (head dim 128) take the
+# eight-wave prefill; these shapes reach it with ragged query and key ends.
+EIGHT_WAVE = [
+    # (B, Hq, Hkv, Nq, Nk, dtype, causal, window_lo, pos0)
+    (1, 16, 4, 32760, 1000, torch.bfloat16, True, 100, 0),
+    (1, 16, 16, 32760, 777, torch.float16, False, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE, ids=[str(i) for i in range(len(EIGHT_WAVE))])
+def test_prefill_eight_wave_grid(case):
+    B, Hq, Hkv, Nq, Nk, dt, causal, wlo, pos0 = case
+    w = Workload("eightwave", B, Hq, Hkv, Nq, Nk, 128, dt, causal=causal, window_lo=wlo,
+                 pos0=pos0)
+    # sampled rows plus the ends of the first and last query tiles of a few heads
+    edge = [h * Nq + i for h in (0, 5, Hq - 1) for i in (0, 1, 99, 100, 255, 256, Nq - 2, Nq - 1)]
+    rows = np.unique(np.concatenate([sample_rows(w, 256), np.array(edge, dtype=np.int64)]))
+    out, _, _, _ = check_workload(w, rows=rows)
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
+
+
 DECODE = []
 for rows_, G in [(1, 1), (2, 2), (4, 2), (8, 4), (4, 8), (1, 16)]:
     for pos0, Nk, wlo in [(4092, 4096, 0), (4092, 4096, 17), (600, 640, 0), (2047, 2051, 64),
