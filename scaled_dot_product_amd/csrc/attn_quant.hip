@@ -314,18 +314,23 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // The int32 scores start from 0x4B400000, the bit pattern of 1.5 * 2^23:
+  // |S| < 2^22, so each accumulator, read as a float, is exactly 1.5 * 2^23 + S
+  // and no int-to-float conversion is needed.
+  i32x16 magic;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) magic[j] = 0x4B400000;
+  // opaque to the compiler: the constant stays in its 16 registers instead of
+  // being copied in again from scalar registers before every tile
+  asm volatile("" : "+v"(magic));
   auto s_mma = [&](int buf, i32x16 (&s)[2]) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[mb][j] = 0;
 #pragma unroll
     for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int r = 32 * mb + col;
         const i32x4 ka = *(const i32x4*)&sk[buf][r * D + 16 * ((2 * k + half) ^ kswz(r))];
-        s[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv[k], s[mb], 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv[k], k == 0 ? magic : s[mb], 0, 0, 0);
       }
   };
 
@@ -340,11 +345,14 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     const float sv_t = Vs[t];
     const float ratio = sref > 0.0f ? fmaxf(sv_t / sref, 9.5367431640625e-7f) : 1.0f;
     const float bias = __builtin_amdgcn_logf(ratio) + (kLog2_448 - kMargin);   // log2
-    float sf[2][16];
+    constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
+    float sf[2][16];                      // kOff + S
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sf[mb][j] = (float)cur[mb][j];
+      for (int j = 0; j < 16; ++j) sf[mb][j] = __builtin_bit_cast(f32x16, cur[mb])[j];
+    // (the whole vector is reinterpreted: a bit cast of one element of the
+    // accumulator vector was miscompiled into copies of element 0)
     const int k0 = 64 * t;
     if ((k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0)) {
 #pragma unroll
@@ -361,7 +369,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sf[0][j]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sf[1][j]);
-    mx = halves_max(mx) * cf;
+    mx = (halves_max(mx) - kOff) * cf;   // exact subtraction
     // the running maximum must be current: every scaled weight stays <= 448
     if (__builtin_amdgcn_ballot_w64(mx > m_run)) {
       asm volatile("" ::: "memory");
@@ -375,6 +383,22 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
       m_run = m_new;
     }
     const float mu = (m_run == -INFINITY ? 0.0f : m_run) - bias;
+    // exponent = S cf - mu = (kOff + S) cf - (kOff cf + mu): one FMA per score.
+    // The rounding of kOff cf + mu shifts every exponent of the tile by at
+    // most 2^-24 |kOff cf + mu| < 0.9 cf + 2^-21, far below the effect of the
+    // INT8 rounding of the scores; it must also stay below the headroom from
+    // 448 up to the E4M3 rounding boundary 464 (0.05 in log2), which holds for
+    // cf < 0.03. Larger factors (from large block maxima or a large scale;
+    // with scale 1/sqrt(128), a product of Q and K block maxima above about
+    // 3800) take the exact form.
+    float C = fmaf(kOff, cf, mu);
+    if (cf >= 0.03f) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sf[mb][j] -= kOff;
+      C = mu;
+    }
 
     // S of tile i + 1 (i8 MFMA) interleaved with the weights of tile i.
     s_mma((i + 1) & 1, nxt);
@@ -387,7 +411,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
         float e[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -mu));
+          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -C));
           ls[k] += e[k];
         }
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
