@@ -214,6 +214,11 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   // exp2 rounds within an ulp or so; lowering the bias by 2^-12 keeps every
   // scaled weight <= 448 (the largest E4M3 magnitude) without a clamp
   constexpr float kMargin = 2.44140625e-4f;
+  // The running maximum may trail the true one by up to kLag powers of two
+  // before O is rescaled; the weights' FP8 scale is lowered by 2^kLag so that
+  // none of them exceeds 448 meanwhile (relative FP8 precision is unchanged,
+  // the smallest weights reach the subnormal range 2 powers of two earlier).
+  constexpr float kLag = 2.0f;
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][64 * D];
   __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * 64];
   __shared__ float sred[4];
@@ -344,7 +349,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     const float cf = fmaxf(cq * Ks[t], 1.17549435e-38f);
     const float sv_t = Vs[t];
     const float ratio = sref > 0.0f ? fmaxf(sv_t / sref, 9.5367431640625e-7f) : 1.0f;
-    const float bias = __builtin_amdgcn_logf(ratio) + (kLog2_448 - kMargin);   // log2
+    const float bias = __builtin_amdgcn_logf(ratio) + (kLog2_448 - kMargin - kLag);   // log2
     constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
     float sf[2][16];                      // kOff + S
 #pragma unroll
@@ -370,8 +375,9 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sf[1][j]);
     mx = (halves_max(mx) - kOff) * cf;   // exact subtraction
-    // the running maximum must be current: every scaled weight stays <= 448
-    if (__builtin_amdgcn_ballot_w64(mx > m_run)) {
+    // the running maximum must be within kLag of the scores: every scaled
+    // weight stays <= 448
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLag)) {
       asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -463,8 +469,8 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   }
 
   const float l = halves_sum(l_run);
-  // undo the fp8 weight scaling: 448 * 2^-margin / s_ref
-  const float inv = l > 0.0f ? (sref * __builtin_amdgcn_exp2f(kMargin) / 448.0f) / l : 0.0f;
+  // undo the fp8 weight scaling: 448 * 2^-(margin + lag) / s_ref
+  const float inv = l > 0.0f ? (sref * __builtin_amdgcn_exp2f(kMargin + kLag) / 448.0f) / l : 0.0f;
   if (qrow < a.Nq) {
     TO* orow = Op + (int64_t)qrow * D;
 #pragma unroll
