@@ -4,8 +4,8 @@
 // section 1 of "Attention kernels on a home RTX 5080": Q and K become
 // symmetric INT8 codes with one fp32 scale per 64-token block of one head,
 // V becomes OCP FP8 E4M3 codes with one scale per 64-token block, and the
-// softmax weights are rounded to E4M3 with a static scale (each weight is at
-// most 1 because the running maximum is always current in this kernel).
+// softmax weights are rounded to E4M3 with a per-key-block scale (each weight
+// is at most 4: the running maximum trails the scores by at most 2 in log2).
 //
 //   quant_int8_kernel   per block: amax, scale = amax/127, inv = 127/amax,
 //                       code = clamp(rint(x*inv), -127, 127)  (bit-exact)
@@ -15,12 +15,12 @@
 //   prefill_quant_kernel
 //     S_int^T = Kc Qc^T              i8 MFMA 32x32x32, exact int32
 //     exponent = S_int * (s_q s_k scale log2 e) - m   (one FMA per score)
-//     P^ = E4M3(448 P s_v / s_ref)   (s_v: the tile's V block scale, s_ref
-//                                     the head's largest; folded into the
-//                                     exponent's bias)
+//     P^ = E4M3(112 P s_v / s_ref)   (s_v: the tile's V block scale, s_ref
+//                                     the largest one the query tile sees;
+//                                     folded into the exponent's bias)
 //     O_acc += Vc^T P^T              fp8 MFMA 32x32x64, fp32 accumulation
 //     l += sum of P (unquantised)
-//   O = O_acc * s_ref / 448 / l.
+//   O = O_acc * s_ref / 112 / l.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
@@ -194,11 +194,11 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
 //
 // The V block scale s_v changes from tile to tile. Rather than rescale the
 // fp32 output by s_v after every tile, each tile's weights are quantised as
-// E4M3(448 P s_v / s_ref) with s_ref the largest V block scale of the head:
-// the factor 448 s_v / s_ref <= 448 goes into the exponent's bias (free),
-// the fp8 products accumulate straight into O, and the epilogue multiplies
-// by s_ref / 448 once. The denominator sums the unquantised weights (the
-// exponentials taken back by the same per-tile factor).
+// E4M3(112 P s_v / s_ref) with s_ref the largest V block scale the query tile
+// sees: the factor 112 s_v / s_ref <= 112 goes into the exponent's bias
+// (free), the fp8 products accumulate straight into O, and the epilogue
+// multiplies by s_ref / 112 once. The denominator sums the unquantised
+// weights (the exponentials taken back by the same per-tile factor).
 template <typename TO, int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
