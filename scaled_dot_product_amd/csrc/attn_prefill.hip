@@ -253,6 +253,20 @@ prefill_kernel(FwdArgs a, int ntq) {
     load_v(t, i & 1);
     apply_mask(cur, t);
 
+    // Weights of one 32-key block of tile i: the B operands of P V (rounded
+    // to the operand type) against the reference mu.
+    auto weights = [&](int mb, float mu_, V8 (&p)[2]) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          p[tt][q] = E::from_float(__builtin_amdgcn_exp2f(fmaf(cur[mb][8 * tt + q], a.c, -mu_)));
+    };
+
+    // First half: P V of tile i - 1 on the MFMA pipe beside the row maxima of
+    // tile i and, speculatively against the current running maximum, the
+    // weights of its first 32 keys (redone in the rare rescale branch), so
+    // that both halves carry about the same vector work.
     if constexpr (!kFirst) pv_mma((i - 1) & 1);
     float mx = cur[0][0];
 #pragma unroll
@@ -260,16 +274,27 @@ prefill_kernel(FwdArgs a, int ntq) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][j]);
     mx = halves_max(mx) * a.c;
+    V8 pa[2], pb[2];
+    weights(0, m_run == -INFINITY ? 0.0f : m_run, pa);
     if constexpr (!kFirst) {
-      // 4 DB MFMAs with the maxima spread between them; transpose reads
+      // 4 DB MFMAs with the vector work spread between them; transpose reads
       // run ahead of the MFMAs that use them.
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPre, 0);
 #pragma unroll
       for (int k = 0; k < 4 * DB; ++k) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (4 * DB), 0);
         if (k < 4 * DB - kVPre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
+    }
+    {
+      // keep the speculative weights in this half (the compiler would sink
+      // them past the branch below)
+      u32x4 w0 = __builtin_bit_cast(u32x4, pa[0]);
+      u32x4 w1 = __builtin_bit_cast(u32x4, pa[1]);
+      asm volatile("" : "+v"(w0), "+v"(w1));
+      pa[0] = __builtin_bit_cast(V8, w0);
+      pa[1] = __builtin_bit_cast(V8, w1);
     }
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
       // rare after the first tiles; the empty asm keeps this a real branch
@@ -284,31 +309,28 @@ prefill_kernel(FwdArgs a, int ntq) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
       m_run = m_new;
+      weights(0, m_run == -INFINITY ? 0.0f : m_run, pa);
     }
     const float mu = m_run == -INFINITY ? 0.0f : m_run;
 
-    // S of tile i + 1 (MFMA) interleaved with the exponentials of tile i.
+    // Second half: S of tile i + 1 (MFMA) beside the weights of the other 32
+    // keys of tile i and the row sums.
     s_mma((i + 1) & 1, nxt);
+    weights(1, mu, pb);
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // the denominator sums the rounded weights the P V product uses
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        V8 p;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          p[q] = E::from_float(__builtin_amdgcn_exp2f(fmaf(cur[mb][8 * tt + q], a.c, -mu)));
-        pprev[mb][tt] = p;
-        // the denominator sums the rounded weights the P V product uses
-        ls[2 * mb + tt] = E::sum8(p, ls[2 * mb + tt]);
-      }
-    // 2*KS MFMAs with the exponentials spread between them; the K reads
-    // run ahead of the MFMAs that use them.
+    for (int tt = 0; tt < 2; ++tt) {
+      ls[tt] = E::sum8(pa[tt], ls[tt]);
+      ls[2 + tt] = E::sum8(pb[tt], ls[2 + tt]);
+    }
+    // 2*KS MFMAs with the vector work spread between them; the K reads run
+    // ahead of the MFMAs that use them.
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKPre, 0);
 #pragma unroll
     for (int k = 0; k < 2 * KS - kKPre; ++k) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 40 / KS, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (2 * KS), 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKPre, 0);
@@ -317,13 +339,13 @@ prefill_kernel(FwdArgs a, int ntq) {
     // past the barrier to their first use in the next step, where the P V
     // MFMAs would wait on them and no MFMA would run beside them.
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        u32x4 w = __builtin_bit_cast(u32x4, pprev[mb][tt]);
-        asm volatile("" : "+v"(w));
-        pprev[mb][tt] = __builtin_bit_cast(V8, w);
-      }
+    for (int tt = 0; tt < 2; ++tt) {
+      u32x4 w0 = __builtin_bit_cast(u32x4, pa[tt]);
+      u32x4 w1 = __builtin_bit_cast(u32x4, pb[tt]);
+      asm volatile("" : "+v"(w0), "+v"(w1));
+      pprev[0][tt] = __builtin_bit_cast(V8, w0);
+      pprev[1][tt] = __builtin_bit_cast(V8, w1);
+    }
 
     vmem_wait_all();   // this wave's direct-to-LDS loads have landed
     __syncthreads();
