@@ -205,6 +205,13 @@ def run_extra(part):
                           "kernel_tops_est": round(wq.flops() / ((ms_q - ms_prep) * 1e-3) / 1e12, 2),
                           "frac_of_fp8_peak": round(wq.flops() / (ms_q * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
         log(f"quant: {ms_q:.3f} ms/call incl. {ms_prep:.3f} ms preparation")
+    elif part == "causal":
+        wc = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_causal_bf16_32760", causal=True)
+        ms_c = bench_prefill(wc, 10, 2)
+        extra["causal"] = {"workload": wc.name, "ms_per_call": round(ms_c, 4),
+                           "tflops": round(wc.flops() / (ms_c * 1e-3) / 1e12, 2),
+                           "frac_of_bf16_peak": round(wc.flops() / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"causal: {ms_c:.3f} ms/call")
     elif part == "sdxl":
         ws_ = WORKLOADS["sdxl_1024px_bf16"]
         ms_s = bench_prefill(ws_, 50, 10)
@@ -254,7 +261,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "quant", "sdxl", "copy"],
+    ap.add_argument("--only", choices=["decode", "quant", "causal", "sdxl", "copy"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -288,7 +295,7 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "sdxl", "decode"):
+        for part in ("quant", "causal", "sdxl", "decode"):
             extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)

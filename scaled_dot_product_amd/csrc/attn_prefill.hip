@@ -74,7 +74,10 @@ prefill_kernel(FwdArgs a, int ntq) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, col = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / ntq, qt = tile - bh * ntq;
+  const int bh = tile / ntq, qt_in = tile - bh * ntq;
+  // Causal rows see more keys the later they sit: a head's heaviest q-tiles
+  // are dispatched first, so the light ones fill the end of the grid.
+  const int qt = a.causal ? ntq - 1 - qt_in : qt_in;
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int q0 = qt * BM;

@@ -45,6 +45,12 @@ def test_video_dit_sampled():
     check_workload(w, rows=sample_rows(w, 256))
 
 
+def test_video_dit_causal_sampled():
+    # causal prefill at video scale (heaviest q-tiles dispatched first)
+    w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_causal", causal=True)
+    check_workload(w, rows=sample_rows(w, 256))
+
+
 def test_video_dit_quant_sampled():
     w = WORKLOADS["video_dit_quant_32760"]
     _, _, rel, _ = check_workload(w, rows=sample_rows(w, 256))
