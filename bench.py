@@ -231,7 +231,43 @@ def run_extra(part):
                           "bytes_per_call": nbytes,
                           "frac_of_hbm_peak_cold": round(nbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
             log(f"{key}: cold {cold_us:.2f} us ({extra[key]['gbs_cold']} GB/s), hot {hot_us:.2f} us")
+        extra["decode"]["sync_us_median"] = round(decode_sync_latency(WORKLOADS["gqa_decode_f16_4096"]), 2)
+        log(f"decode: one synchronous call {extra['decode']['sync_us_median']} us (host wall clock)")
+        sweep = {}
+        for nk in (4096, 8192, 16384, 32768, 65536):
+            wd = WORKLOADS["gqa_decode_f16_4096"].variant(Nk=nk, pos0=nk - 4)
+            per = 2 * wd.B * wd.Hkv * nk * wd.D * 2
+            nbuf = max(3, min(48, -(-640_000_000 // per)))   # > 600 MB of caches: cold
+            cold_us, _, nbytes = bench_decode(wd, nbuf=nbuf, reps=10)
+            sweep[str(nk)] = {"us_cold": round(cold_us, 2),
+                              "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1)}
+            log(f"decode sweep Nk={nk}: {cold_us:.2f} us, {sweep[str(nk)]['gbs_cold']} GB/s")
+        extra["decode_kv_sweep"] = sweep
     return extra
+
+
+def decode_sync_latency(w, calls=50):
+    """Median host wall time of one decode call followed by a device synchronize."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import make_qkv
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_qkv(w))
+    out = torch.empty_like(q)
+    ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                    window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    ts = []
+    for i in range(calls + 5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, scale=w.scale,
+                 out=out, workspace=ws)
+        torch.cuda.synchronize()
+        if i >= 5:
+            ts.append((time.perf_counter() - t0) * 1e6)
+    ts.sort()
+    return ts[len(ts) // 2]
 
 
 def recorded_traffic(record: str):

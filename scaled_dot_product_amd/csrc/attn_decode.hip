@@ -24,7 +24,7 @@ namespace attn {
 
 namespace {
 
-constexpr int kMaxSplits = 64;     // workgroups per key/value head, at most
+constexpr int kMaxSplits = 32;     // workgroups per key/value head, at most
 
 struct DecodeArgs {
   int rows, t_lo, t_hi, nsplit, tiles_per_wg;
