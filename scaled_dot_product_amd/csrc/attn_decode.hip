@@ -4,9 +4,10 @@
 // byte, so it is bound by HBM bandwidth and latency, not by the matrix cores.
 // All G * Nq query rows that share a key/value head (G = Hq / Hkv) are packed
 // into the 32 columns of one MFMA block, so each K/V byte feeds every one of
-// them. The visible keys are cut into 64-key tiles; each wave takes one tile
-// at a time (K straight from global memory into A-operand registers, V
-// transposed through a private LDS slab) and keeps an online-softmax partial
+// them. The visible keys are cut into 64-key tiles; each wave streams its own
+// tiles through a private pair of LDS tiles (direct global-to-LDS loads, the
+// prefill's swizzles; V^T operands by transpose reads; the next K tile loads
+// while this one's softmax and P V run) and keeps an online-softmax partial
 // (O_s, m_s, l_s); the waves of a workgroup merge theirs in LDS and publish one
 // partial per workgroup. The last workgroup of a key/value head to publish
 // merges all partials of that head with log-sum-exp weights and writes O, so
@@ -63,20 +64,16 @@ __device__ __forceinline__ float get1(const float* src) {
 }
 
 // Arrival counting for the fused merge. The counter of a key/value head is
-// (generation << 24) | arrivals. At kernel start (off the critical path, while
-// the tile loads are in flight) one thread of each workgroup claims the
-// counter for this call: a counter whose tag is not this call's generation
-// (left by an earlier call, or uninitialised workspace) is swapped for
-// (generation << 24). A failed swap means another workgroup already claimed
-// it, so at most one swap per workgroup is tried. Arrival is then a single
-// atomic add; the workgroup that sees nsplit - 1 earlier arrivals is last.
-// It resets the counter to 0, a tag no call uses, so replays of a captured
-// graph (same generation) claim it again. Claims all precede the reset, as
-// every workgroup claims before it arrives.
-__device__ void claim_counter(unsigned long long* c, unsigned long long gen) {
-  const unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((cur >> 24) != gen) atomicCAS(c, cur, gen << 24);
-}
+// (generation << 24) | arrivals. One thread of each workgroup claims it for
+// this call in two parts kept off the critical path: it reads the counter
+// behind its tile loads, and after its tiles, if the tag read is not this
+// call's generation (left by an earlier call, or uninitialised workspace), it
+// swaps the value read for (generation << 24). A failed swap means another
+// workgroup already claimed it. Arrival is then a single atomic add; the
+// workgroup that sees nsplit - 1 earlier arrivals is last. It resets the
+// counter to 0, a tag no call uses, so replays of a captured graph (same
+// generation) claim it again. Every swap precedes its own workgroup's
+// arrival, so all of them precede the reset.
 __device__ bool arrive_last(unsigned long long* c, int nsplit) {
   const unsigned long long old = atomicAdd(c, 1ull);
   return (int)(old & 0xffffffull) == nsplit - 1;
@@ -89,15 +86,20 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   using V8 = typename E::vec8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int VLD = 64 + 8;
-  constexpr int UV = D / 32;               // V loads per lane per tile, in groups of 4 keys
-  // Per-wave V^T slabs; reused after a barrier for the cross-wave merge.
-  constexpr int SLAB = D * VLD * 2;        // bytes per wave
-  constexpr int MERGE = kWaves * 32 * D * 4 + 2 * kWaves * 32 * 4;
-  constexpr int LDS_BYTES = (kWaves * SLAB > MERGE) ? kWaves * SLAB : MERGE;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;            // rows one 64-lane direct load covers
+  constexpr int NL = 64 / RPI;             // direct loads per 64-row tile
+  constexpr int TILE = 64 * D;             // elements of one K or V tile
+  // Each wave streams its own tiles through a K and a V tile of its own in
+  // LDS. The cross-wave merge reuses the K tiles' bytes (32 x D floats per
+  // wave).
+  __shared__ __attribute__((aligned(16))) T sk_all[kWaves * TILE];
+  __shared__ __attribute__((aligned(16))) T sv_all[kWaves * TILE];
+  __shared__ float sml[2 * kWaves * 32];
+  static_assert(sizeof(T) * TILE == 32 * D * sizeof(float), "merge area must fit a K tile");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -105,7 +107,8 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   const int64_t kvbase = (int64_t)bg * a.Nk * D;
   const T* __restrict__ Kp = (const T*)a.k + kvbase;
   const T* __restrict__ Vp = (const T*)a.v + kvbase;
-  T* slab = (T*)(lds + wave * SLAB);
+  T* sk = sk_all + wave * TILE;
+  T* sv = sv_all + wave * TILE;
 
   // Column -> (query head within the group, row): n = hh * Nq + i. Columns past
   // the packed rows read row 0 and are masked out.
@@ -117,125 +120,143 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(V8, ld16(Qrow + 16 * ks + 8 * half));
 
+  // Tiles go straight into LDS (16 bytes per lane, 1 KB per instruction) with
+  // the XOR chunk swizzles and K row order of the prefill: K row r holds key
+  // (r & ~31) | swap23(r & 31), V row r key r; rows past Nk clamp to the last.
+  auto kswz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  auto load_k = [&](int t) {
+    const char* base = (const char*)(Kp + (int64_t)64 * t * D);
+    const int last = a.Nk - 1 - 64 * t;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r = RPI * u + lane / CPR, pos = lane % CPR;
+      const int kk = (r & ~31) | swap23(r & 31);
+      load_to_lds16(base, (uint32_t)(min(kk, last) * (D * 2) + 16 * (pos ^ kswz(r))), sk + RPI * u * D);
+    }
+  };
+  auto load_v = [&](int t) {
+    const char* base = (const char*)(Vp + (int64_t)64 * t * D);
+    const int last = a.Nk - 1 - 64 * t;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r = RPI * u + lane / CPR, pos = lane % CPR;
+      load_to_lds16(base, (uint32_t)(min(r, last) * (D * 2) + 16 * (pos ^ vswz(r))), sv + RPI * u * D);
+    }
+  };
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  bool claimed = false;   // uniform: the counter is claimed after the first loads
 
   // This workgroup's tiles: [t0, t1); wave w takes t0 + w, t0 + w + kWaves, ...
+  // K of the next tile is loaded once S of this one has read its K tile, V
+  // of the next once P V has read its V tile.
   const int t0 = p.t_lo + split * p.tiles_per_wg;
   const int t1 = min(t0 + p.tiles_per_wg, p.t_hi);
-  const int kg = lane & 15, c0 = lane >> 4;
-  for (int tb = t0; tb < t1; tb += kWaves) {
-    const int t = tb + wave;
-    const bool has_tile = t < t1;
+  int t = t0 + wave;
+  if (t < t1) {
+    load_k(t);
+    load_v(t);
+  }
+  // Claim the arrival counter in two parts: its read is issued here, behind
+  // the tile loads, and the swap (if any) after the tiles, when the read has
+  // long returned; neither waits on the critical path.
+  unsigned long long ctr_seen = 0;
+  if (tid == 0) ctr_seen = __hip_atomic_load(p.ctr + bg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto tile = [&](int t) {
     const int k0 = t * 64;
-    // Phase 1: every load of the tile issued back to back. Rows past Nk are
-    // clamped to a real row (finite values) and masked below.
-    u32x4 kreg[2][KS];
-    if (has_tile) {
+    const bool more = t + kWaves < t1;
+    // this wave's K and V tiles (and everything loaded before) have landed;
+    // the direct loads are not tracked by the compiler, so this wait is ours
+    vmem_wait_all();
+    // S^T = K Q^T: four independent accumulators (even/odd k-steps).
+    f32x16 s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[mb][h2][j] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int key = min(k0 + 32 * mb + swap23(col), a.Nk - 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kreg[mb][ks] = ld16(Kp + (int64_t)key * D + 16 * ks + 8 * half);
+        const int r = 32 * mb + col;
+        const V8 ka = *(const V8*)&sk[r * D + 8 * ((2 * ks + half) ^ kswz(r))];
+        s[mb][ks & 1] = E::mma(ka, qv[ks], s[mb][ks & 1]);
       }
-      u32x4 vreg[UV][4];
+    // every K read of this wave has returned before the next K tile lands
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (more) load_k(t + kWaves);
+    float sc[2][16];
 #pragma unroll
-      for (int u = 0; u < UV; ++u)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = min(k0 + 4 * kg + r, a.Nk - 1);
-          vreg[u][r] = ld16(Vp + (int64_t)key * D + 8 * (c0 + 4 * u));
-        }
-      // claim while this wave's tile loads are in flight (its wait on the
-      // counter read then overlaps the wait on the tile)
-      if (!claimed && tid == 0) claim_counter(p.ctr + bg, p.gen);
-      // V^T into this wave's slab.
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const int cc = c0 + 4 * u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x2 pk;
-          pk[0] = __builtin_amdgcn_perm(vreg[u][1][e >> 1], vreg[u][0][e >> 1], sel);
-          pk[1] = __builtin_amdgcn_perm(vreg[u][3][e >> 1], vreg[u][2][e >> 1], sel);
-          *(u32x2*)&slab[(8 * cc + e) * VLD + 4 * kg] = pk;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
+        const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
+                         (!a.causal || key <= a.pos0 + qi);
+        sc[mb][j] = vis ? s[mb][0][j] + s[mb][1][j] : -INFINITY;
       }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[1][j]);
+    mx = halves_max(mx) * a.c;
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    const float mu = m == -INFINITY ? 0.0f : m;
+    V8 pv[2][2];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[mb][8 * tt + i], a.c, -mu));
+          lsum += e;
+          pv[mb][tt][i] = E::from_float(e);
+        }
+    l = l * alpha + halves_sum(lsum);
+    // O^T += V^T P^T; the V^T operands come through transpose reads (as in the
+    // prefill): lane r of a 16-lane group names key kb + r/4 at channel d0 + 4 (r % 4).
+    const int gq = lane >> 4, rr = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          s16x4 part[2];
+#pragma unroll
+          for (int rd = 0; rd < 2; ++rd) {
+            const int key = 32 * mb + 16 * tt + 8 * (gq >> 1) + 4 * rd + (rr >> 2);
+            const int d0 = 32 * db + 16 * (gq & 1) + 4 * (rr & 3);
+            part[rd] = lds_read_tr16(&sv[key * D + 8 * ((d0 >> 3) ^ vswz(key)) + (d0 & 7)]);
+          }
+          const s16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                              part[1][0], part[1][1], part[1][2], part[1][3]};
+          oacc[db] = E::mma(__builtin_bit_cast(V8, both), pv[mb][tt], oacc[db]);
+        }
     }
-    __syncthreads();
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): V reads returned
+      load_v(t + kWaves);
+    }
+  };
+  for (; t < t1; t += kWaves) tile(t);
+  if (tid == 0 && (ctr_seen >> 24) != p.gen) atomicCAS(p.ctr + bg, ctr_seen, p.gen << 24);
+  __syncthreads();   // every wave is done with its tiles before the merge reuses LDS
 
-    // Phase 2: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-    if (has_tile) {
-      // four independent accumulators (even/odd k-steps) shorten the MFMA chains
-      f32x16 s[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) s[mb][h2][j] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          s[mb][ks & 1] = E::mma(__builtin_bit_cast(V8, kreg[mb][ks]), qv[ks], s[mb][ks & 1]);
-      float sc[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-          const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
-                           (!a.causal || key <= a.pos0 + qi);
-          sc[mb][j] = vis ? s[mb][0][j] + s[mb][1][j] : -INFINITY;
-        }
-      float mx = sc[0][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[0][j]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[1][j]);
-      mx = halves_max(mx) * a.c;
-      const float m_new = fmaxf(m, mx);
-      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      const float mu = m == -INFINITY ? 0.0f : m;
-      V8 pv[2][2];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sc[mb][8 * tt + i], a.c, -mu));
-            lsum += e;
-            pv[mb][tt][i] = E::from_float(e);
-          }
-      l = l * alpha + halves_sum(lsum);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const V8 va = *(const V8*)&slab[(32 * db + col) * VLD + 32 * mb + 16 * tt + 8 * half];
-            oacc[db] = E::mma(va, pv[mb][tt], oacc[db]);
-          }
-      }
-    }
-    __syncthreads();
-    claimed = true;
-  }
-  // A workgroup without tiles still claims before it arrives.
-  if (!claimed && tid == 0) claim_counter(p.ctr + bg, p.gen);
 
   // 1. Publish this workgroup's partial.
   const int64_t pbase = ((int64_t)bg * p.nsplit + split) * p.rows;
@@ -259,9 +280,9 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
     }
   } else {
     // Merge the waves in LDS, in a fixed order, then publish.
-    float* so = (float*)lds;                              // [wave][32][D]
-    float* sm = so + kWaves * 32 * D;                     // [wave][32]
-    float* sl = sm + kWaves * 32;                         // [wave][32]
+    float* so = (float*)sk_all;                           // [wave][32][D]
+    float* sm = sml;                                      // [wave][32]
+    float* sl = sml + kWaves * 32;                        // [wave][32]
     if (cvalid) {
       if (half == 0) {
         sm[wave * 32 + col] = m;
