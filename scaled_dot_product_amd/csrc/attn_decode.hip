@@ -446,7 +446,10 @@ DecodePlan decode_plan(const FwdArgs& a) {
   // tiles. Fewer, fuller workgroups keep the final merge (on the critical
   // path, in the last workgroup) short.
   p.waves = 4;
-  const int per_wave = (p.ntiles + p.waves * kMaxSplits - 1) / (p.waves * kMaxSplits);
+  // Up to two tiles per wave, 16 splits merge faster than 32 splits run a
+  // second tile: 32 only for longer ranges.
+  const int cap = p.ntiles <= 2 * p.waves * 16 ? 16 : kMaxSplits;
+  const int per_wave = (p.ntiles + p.waves * cap - 1) / (p.waves * cap);
   p.tiles_per_wg = p.waves * (per_wave < 1 ? 1 : per_wave);
   p.nsplit = (p.ntiles + p.tiles_per_wg - 1) / p.tiles_per_wg;
   if (p.nsplit < 1) p.nsplit = 1;
