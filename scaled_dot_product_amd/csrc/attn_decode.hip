@@ -79,6 +79,160 @@ __device__ bool arrive_last(unsigned long long* c, int nsplit) {
   return (int)(old & 0xffffffull) == nsplit - 1;
 }
 
+// After the tiles: the counter claim, the merge of the waves' partials in LDS
+// (so: kWaves x 32 x D floats, sml: 2 x kWaves x 32 floats), the workgroup's
+// partial published, the arrival, and in the last workgroup of the KV head
+// the merge of all splits into O.
+template <typename TO, int D, int kWaves>
+__device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs& p, float m,
+                                              float l, f32x16 (&oacc)[D / 32], float* so_base,
+                                              float* sml, unsigned long long ctr_seen) {
+  constexpr int DB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int split = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const bool cvalid = col < p.rows;
+  if (tid == 0 && (ctr_seen >> 24) != p.gen) atomicCAS(p.ctr + bg, ctr_seen, p.gen << 24);
+  __syncthreads();   // every wave is done with its tiles before the merge reuses LDS
+
+
+  // 1. Publish this workgroup's partial.
+  const int64_t pbase = ((int64_t)bg * p.nsplit + split) * p.rows;
+  if constexpr (kWaves == 1) {
+    // One wave: its partial goes straight from registers to the workspace.
+    if (cvalid) {
+      if (half == 0) {
+        put1(&p.mpart[pbase + col], m);
+        put1(&p.lpart[pbase + col], l);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d = 32 * db + 8 * a4 + 4 * half;
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = oacc[db][4 * a4 + r];
+          put4(&p.opart[(pbase + col) * D + d], v);
+        }
+    }
+  } else {
+    // Merge the waves in LDS, in a fixed order, then publish.
+    float* so = so_base;                                  // [wave][32][D]
+    float* sm = sml;                                      // [wave][32]
+    float* sl = sml + kWaves * 32;                        // [wave][32]
+    if (cvalid) {
+      if (half == 0) {
+        sm[wave * 32 + col] = m;
+        sl[wave * 32 + col] = l;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d = 32 * db + 8 * a4 + 4 * half;
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = oacc[db][4 * a4 + r];
+          *(f32x4*)&so[(wave * 32 + col) * D + d] = v;
+        }
+    }
+    __syncthreads();
+    constexpr int SLOTS = D / 4;   // threads per row
+    for (int idx = tid; idx < p.rows * SLOTS; idx += 64 * kWaves) {
+      const int n = idx / SLOTS, d = (idx - n * SLOTS) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 32 + n]);
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      float L = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = __builtin_amdgcn_exp2f(sm[w * 32 + n] - M);
+          L += f * sl[w * 32 + n];
+          const f32x4 v = *(const f32x4*)&so[(w * 32 + n) * D + d];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] += f * v[r];
+        }
+      }
+      put4(&p.opart[(pbase + n) * D + d], acc);
+      if (d == 0) {
+        put1(&p.mpart[pbase + n], M);
+        put1(&p.lpart[pbase + n], L);
+      }
+    }
+  }
+
+  // 2. Arrive; the last workgroup of this key/value head merges all splits.
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);   // every partial store of this thread acknowledged
+  __syncthreads();
+  if (tid == 0) s_last = arrive_last(p.ctr + bg, p.nsplit);
+  __syncthreads();
+  if (!s_last) return;
+
+  // Final merge, one thread per (row, 4 channels): all loads of a chunk of
+  // splits first (one memory round trip per 16 splits), then an online
+  // log-sum-exp merge in registers, in split order.
+  constexpr int NT = 64 * kWaves;
+  constexpr int SLOTS = D / 4;
+  constexpr int CH = 16;
+  const int ns = p.nsplit, rows = p.rows;
+  const int64_t hbase = (int64_t)bg * ns * rows;
+  for (int idx = tid; idx < rows * SLOTS; idx += NT) {
+    const int n = idx / SLOTS, d = (idx - n * SLOTS) * 4;
+    float M = -INFINITY, L = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < ns; s0 += CH) {
+      float mv[CH], lv[CH];
+      f32x4 ov[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int sp = min(s0 + u, ns - 1);
+        const int64_t r = hbase + (int64_t)sp * rows + n;
+        mv[u] = get1(&p.mpart[r]);
+        lv[u] = get1(&p.lpart[r]);
+        ov[u] = get4(&p.opart[r * D + d]);
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        if (s0 + u >= ns || mv[u] == -INFINITY) continue;
+        if (mv[u] > M) {
+          const float f = __builtin_amdgcn_exp2f(M - mv[u]);   // 0 while M = -inf
+          L = L * f + lv[u];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] = acc[c] * f + ov[u][c];
+          M = mv[u];
+        } else {
+          const float f = __builtin_amdgcn_exp2f(mv[u] - M);
+          L += f * lv[u];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] += f * ov[u][c];
+        }
+      }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int hh2 = n / a.Nq, qi2 = n - hh2 * a.Nq;
+    TO* orow = (TO*)a.o + (((int64_t)b * a.Hq + g * G + hh2) * a.Nq + qi2) * D + d;
+    if constexpr (sizeof(TO) == 4) {
+      f32x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = acc[c] * inv;
+      *(f32x4*)orow = o;
+    } else {
+      TO o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = Elem<TO>::from_float(acc[c] * inv);
+      *(u32x2*)orow = *(const u32x2*)o;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(p.ctr + bg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T, typename TO, int D, int kWaves>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves)))
 decode_kernel(FwdArgs a, DecodeArgs p) {
@@ -254,142 +408,7 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
     }
   };
   for (; t < t1; t += kWaves) tile(t);
-  if (tid == 0 && (ctr_seen >> 24) != p.gen) atomicCAS(p.ctr + bg, ctr_seen, p.gen << 24);
-  __syncthreads();   // every wave is done with its tiles before the merge reuses LDS
-
-
-  // 1. Publish this workgroup's partial.
-  const int64_t pbase = ((int64_t)bg * p.nsplit + split) * p.rows;
-  if constexpr (kWaves == 1) {
-    // One wave: its partial goes straight from registers to the workspace.
-    if (cvalid) {
-      if (half == 0) {
-        put1(&p.mpart[pbase + col], m);
-        put1(&p.lpart[pbase + col], l);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d = 32 * db + 8 * a4 + 4 * half;
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = oacc[db][4 * a4 + r];
-          put4(&p.opart[(pbase + col) * D + d], v);
-        }
-    }
-  } else {
-    // Merge the waves in LDS, in a fixed order, then publish.
-    float* so = (float*)sk_all;                           // [wave][32][D]
-    float* sm = sml;                                      // [wave][32]
-    float* sl = sml + kWaves * 32;                        // [wave][32]
-    if (cvalid) {
-      if (half == 0) {
-        sm[wave * 32 + col] = m;
-        sl[wave * 32 + col] = l;
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d = 32 * db + 8 * a4 + 4 * half;
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = oacc[db][4 * a4 + r];
-          *(f32x4*)&so[(wave * 32 + col) * D + d] = v;
-        }
-    }
-    __syncthreads();
-    constexpr int SLOTS = D / 4;   // threads per row
-    for (int idx = tid; idx < p.rows * SLOTS; idx += 64 * kWaves) {
-      const int n = idx / SLOTS, d = (idx - n * SLOTS) * 4;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 32 + n]);
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      float L = 0.0f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float f = __builtin_amdgcn_exp2f(sm[w * 32 + n] - M);
-          L += f * sl[w * 32 + n];
-          const f32x4 v = *(const f32x4*)&so[(w * 32 + n) * D + d];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] += f * v[r];
-        }
-      }
-      put4(&p.opart[(pbase + n) * D + d], acc);
-      if (d == 0) {
-        put1(&p.mpart[pbase + n], M);
-        put1(&p.lpart[pbase + n], L);
-      }
-    }
-  }
-
-  // 2. Arrive; the last workgroup of this key/value head merges all splits.
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);   // every partial store of this thread acknowledged
-  __syncthreads();
-  if (tid == 0) s_last = arrive_last(p.ctr + bg, p.nsplit);
-  __syncthreads();
-  if (!s_last) return;
-
-  // Final merge, one thread per (row, 4 channels): all loads of a chunk of
-  // splits first (one memory round trip per 16 splits), then an online
-  // log-sum-exp merge in registers, in split order.
-  constexpr int NT = 64 * kWaves;
-  constexpr int SLOTS = D / 4;
-  constexpr int CH = 16;
-  const int ns = p.nsplit, rows = p.rows;
-  const int64_t hbase = (int64_t)bg * ns * rows;
-  for (int idx = tid; idx < rows * SLOTS; idx += NT) {
-    const int n = idx / SLOTS, d = (idx - n * SLOTS) * 4;
-    float M = -INFINITY, L = 0.0f;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < ns; s0 += CH) {
-      float mv[CH], lv[CH];
-      f32x4 ov[CH];
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int sp = min(s0 + u, ns - 1);
-        const int64_t r = hbase + (int64_t)sp * rows + n;
-        mv[u] = get1(&p.mpart[r]);
-        lv[u] = get1(&p.lpart[r]);
-        ov[u] = get4(&p.opart[r * D + d]);
-      }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (s0 + u >= ns || mv[u] == -INFINITY) continue;
-        if (mv[u] > M) {
-          const float f = __builtin_amdgcn_exp2f(M - mv[u]);   // 0 while M = -inf
-          L = L * f + lv[u];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] = acc[c] * f + ov[u][c];
-          M = mv[u];
-        } else {
-          const float f = __builtin_amdgcn_exp2f(mv[u] - M);
-          L += f * lv[u];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] += f * ov[u][c];
-        }
-      }
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const int hh2 = n / a.Nq, qi2 = n - hh2 * a.Nq;
-    TO* orow = (TO*)a.o + (((int64_t)b * a.Hq + g * G + hh2) * a.Nq + qi2) * D + d;
-    if constexpr (sizeof(TO) == 4) {
-      f32x4 o;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = acc[c] * inv;
-      *(f32x4*)orow = o;
-    } else {
-      TO o[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = Elem<TO>::from_float(acc[c] * inv);
-      *(u32x2*)orow = *(const u32x2*)o;
-    }
-  }
-  if (tid == 0) __hip_atomic_store(p.ctr + bg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  decode_finish<TO, D, kWaves>(a, p, m, l, oacc, (float*)sk_all, sml, ctr_seen);
 }
 
 // A different generation for every launch, from a per-process random start
