@@ -12,11 +12,14 @@ the definitions and the passages they follow):
 * :func:`quant_int8`, :func:`quant_e4m3` — per-64-token-block codes + scales.
 * :func:`e4m3_encode`, :func:`e4m3_decode` — the OCP E4M3 format.
 * :func:`attn_quant` — quantised-mode emulation (diagnostic).
+* :func:`attn_kvq` — exact attention over a quantised KV cache (codes + scales).
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and library special cases. ``attn_quant`` is
 pinned only through closed-form special cases (uniform scores; exactly
-representable inputs) — its general output has no independent reference.
+representable inputs) — its general output has no independent reference. ``attn_kvq`` is pinned
+against :func:`attn` on exactly representable caches (values decoded by
+torch's float8 cast), a uniform-weight closed form and the grid case of Q.
 """
 from __future__ import annotations
 
@@ -59,6 +62,9 @@ def _load():
         lib.oracle_attn_quant.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
                                           d, vp, i64, vp, i]
         lib.oracle_attn_quant.restype = i
+        lib.oracle_attn_kvq.argtypes = [vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+                                        d, i, vp, i64, vp, i]
+        lib.oracle_attn_kvq.restype = i
         lib.oracle_quant_int8.argtypes = [vp, i, i64, i, i, vp, vp]
         lib.oracle_quant_int8.restype = i
         lib.oracle_quant_e4m3.argtypes = [vp, i, i64, i, i, vp, vp]
@@ -140,6 +146,42 @@ def attn_quant(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None,
         out.ctypes.data, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_attn_quant failed")
+    return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+def attn_kvq(q, k_codes, k_scales, v_codes, v_scales, *, scale, causal=False, window_lo=0,
+             pos0=0, quant_q=False, rows=None, nthreads=None):
+    """Exact fp64 attention over a quantised KV cache (see oracle.c).
+
+    q: [B,Hq,Nq,D] torch (fp32/f16/bf16); k_codes int8 and v_codes uint8 (E4M3)
+    [B,Hkv,Nk,D]; k_scales, v_scales float32 [B,Hkv,ceil(Nk/64)] (numpy or torch).
+    quant_q: use Q's per-block INT8 dequantisation instead of Q. Same return
+    conventions as attn().
+    """
+    q = _cpu(q)
+    kc = np.ascontiguousarray(np.asarray(k_codes.cpu() if hasattr(k_codes, "cpu") else k_codes, dtype=np.int8))
+    vc = np.ascontiguousarray(np.asarray(v_codes.cpu() if hasattr(v_codes, "cpu") else v_codes, dtype=np.uint8))
+    ks = np.ascontiguousarray(np.asarray(k_scales.cpu() if hasattr(k_scales, "cpu") else k_scales, dtype=np.float32))
+    vs = np.ascontiguousarray(np.asarray(v_scales.cpu() if hasattr(v_scales, "cpu") else v_scales, dtype=np.float32))
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = kc.shape
+    nblk = (Nk + 63) // 64
+    if vc.shape != kc.shape or ks.shape != (B, Hkv, nblk) or vs.shape != (B, Hkv, nblk):
+        raise ValueError("codes [B,Hkv,Nk,D] and scales [B,Hkv,ceil(Nk/64)] expected")
+    if rows is None:
+        nrows, rows_arr = B * Hq * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_attn_kvq(
+        q.data_ptr(), DTYPE_CODE[q.dtype], kc.ctypes.data, ks.ctypes.data, vc.ctypes.data,
+        vs.ctypes.data, B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0),
+        float(scale), int(bool(quant_q)),
+        None if rows_arr is None else rows_arr.ctypes.data, nrows, out.ctypes.data,
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_kvq rejected the arguments")
     return out.reshape(B, Hq, Nq, D) if rows is None else out
 
 

@@ -28,6 +28,9 @@
  *   oracle_attn_quant   the quantised-mode emulation: exact attention on the
  *                       dequantised Q, K, V with every softmax weight passed
  *                       through E4M3 at the static scale 448 (a diagnostic).
+ *   oracle_attn_kvq     exact attention over a quantised KV cache: K and V
+ *                       given as per-block INT8 / E4M3 codes and scales, Q as
+ *                       is or through its own per-block INT8 codes.
  *
  * Readings taken where the pages are silent (listed again in the design
  * notes): query row i sits at absolute position pos0 + i and key j at j; a
@@ -451,6 +454,52 @@ int oracle_attn_quant(const void* q, const void* k, const void* v, int dtype,
     J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
     J.out = out;
     J.qhat = qh; J.khat = kh; J.vhat = vh; J.quant_p = 1;
+    rc = run_attn(&J, nthreads);
+  }
+  free(qh); free(kh); free(vh);
+  return rc;
+}
+
+/*
+ * Attention over a quantised KV cache: the INT8-QK / FP8-PV recipe of the
+ * table in section 1 of "Attention kernels on a home RTX 5080" with K and V
+ * stored as codes. Key j of key/value head (b, g) is
+ *   K[j][d] = kc[j][d] * ks[b][g][j / 64],  V[j][d] = E4M3(vc[j][d]) * vs[b][g][j / 64]
+ * (codes [B][Hkv][Nk][D], scales [B][Hkv][ceil(Nk/64)] fp32). The result is
+ * exact attention (arguments and conventions of oracle_attn) on these K, V
+ * and on Q as given (quant_q = 0) or on the dequantisation of Q's per-block
+ * INT8 codes (quant_q = 1, oracle_quant_int8's recipe).
+ */
+int oracle_attn_kvq(const void* q, int dtype, const int8_t* kc, const float* ks,
+                    const uint8_t* vc, const float* vs,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                    int causal, int window_lo, int pos0, double scale, int quant_q,
+                    const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+  int nblk = (Nk + 63) / 64;
+  double* qh = quant_q ? (double*)malloc(sizeof(double) * (size_t)nq) : NULL;
+  double* kh = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* vh = (double*)malloc(sizeof(double) * (size_t)nk);
+  int rc = -1;
+  if (kh && vh && (!quant_q || qh) &&
+      (!quant_q || dequant_int8(q, dtype, (int64_t)B * Hq, Nq, D, qh) == 0)) {
+    for (int64_t e = 0; e < nk; ++e) {
+      int64_t bg = e / ((int64_t)Nk * D);
+      int tok = (int)((e / D) % Nk);
+      kh[e] = (double)kc[e] * (double)ks[bg * nblk + tok / 64];
+      vh[e] = (double)oracle_e4m3_decode(vc[e]) * (double)vs[bg * nblk + tok / 64];
+    }
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.dtype = dtype;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+    J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale;
+    J.rows = rows;
+    J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+    J.out = out;
+    J.qhat = qh; J.khat = kh; J.vhat = vh;
     rc = run_attn(&J, nthreads);
   }
   free(qh); free(kh); free(vh);

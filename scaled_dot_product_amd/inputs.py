@@ -34,7 +34,7 @@ class Workload:
     causal: bool = False
     window_lo: int = 0
     pos0: int = 0
-    mode: int = 0          # 0 exact, 1 INT8-QK / FP8-PV
+    mode: int = 0          # 0 exact, 1 INT8-QK / FP8-PV, 2 decode over an INT8-K / E4M3-V cache
     scale: float = field(default=float("nan"))
 
     def __post_init__(self):
@@ -76,6 +76,9 @@ WORKLOADS = {
     # few-row GQA decode against an f16 KV cache, bottom-right causal
     "gqa_decode_f16_4096": Workload("gqa_decode_f16_4096", 1, 16, 8, 4, 4096, 128,
                                     torch.float16, causal=True, pos0=4092),
+    # the same decode against a quantised cache (INT8 K, E4M3 V, per-64-key scales)
+    "gqa_decode_kvq_f16_4096": Workload("gqa_decode_kvq_f16_4096", 1, 16, 8, 4, 4096, 128,
+                                        torch.float16, causal=True, pos0=4092, mode=2),
     # SDXL-style 1024px self-attention (64x64 latent tokens)
     "sdxl_1024px_bf16": Workload("sdxl_1024px_bf16", 2, 10, 10, 4096, 4096, 64,
                                  torch.bfloat16),
@@ -101,6 +104,31 @@ def make_qkv(w: Workload, seeds=(SEED_Q, SEED_K, SEED_V)):
     return (normal(w.q_shape, seeds[0], w.dtype),
             normal(w.kv_shape, seeds[1], w.dtype),
             normal(w.kv_shape, seeds[2], w.dtype))
+
+
+def make_kv_codes(w: Workload, seeds=(SEED_K, SEED_V)):
+    """A synthetic quantised KV cache of shape w.kv_shape (CPU tensors).
+
+    K codes are int8 samples of a discretised normal (sigma 40, clipped to
+    +-127) and V codes float8_e4m3fn casts of normal samples scaled to sigma 100
+    (clipped to +-448, stored as uint8 bytes): the spread of codes that blocks of
+    N(0,1) data give. Block scales are 4.5/127 and 4.5/448 (about the block
+    maximum of N(0,1) data over the code range) times exp(0.1 N(0,1)) per
+    64-key block. Returns k_codes int8, k_scales fp32 [B,Hkv,ceil(Nk/64)],
+    v_codes uint8, v_scales fp32.
+    """
+    nblk = (w.Nk + 63) // 64
+    sshape = (w.B, w.Hkv, nblk)
+    rk = np.random.default_rng(seeds[0])
+    kc = np.clip(np.rint(rk.standard_normal(size=w.kv_shape, dtype=np.float32) * 40.0),
+                 -127, 127).astype(np.int8)
+    ks = (4.5 / 127.0) * np.exp(0.1 * rk.standard_normal(size=sshape)).astype(np.float32)
+    rv = np.random.default_rng(seeds[1])
+    vf = np.clip(rv.standard_normal(size=w.kv_shape, dtype=np.float32) * 100.0, -448.0, 448.0)
+    vc = torch.from_numpy(vf).to(torch.float8_e4m3fn).view(torch.uint8)
+    vs = (4.5 / 448.0) * np.exp(0.1 * rv.standard_normal(size=sshape)).astype(np.float32)
+    return (torch.from_numpy(kc), torch.from_numpy(ks.astype(np.float32)), vc,
+            torch.from_numpy(vs.astype(np.float32)))
 
 
 def sample_rows(w: Workload, n: int = 256, seed: int = 7) -> np.ndarray:

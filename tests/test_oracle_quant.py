@@ -208,3 +208,96 @@ def test_quant_emulation_error_matches_page_figure():
     qe = oracle.attn_quant(q, k, v, scale=w.scale, rows=rows)
     err = np.linalg.norm(qe - ex) / np.linalg.norm(ex)
     assert lo <= err <= hi, err
+
+
+# ---- attention over a quantised KV cache --------------------------------------
+
+def _f8_values(codes):
+    """E4M3 code bytes -> values through torch's float8_e4m3fn (a library cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(codes, dtype=np.uint8)))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _random_cache(rng, B, Hkv, Nk, D):
+    nblk = (Nk + 63) // 64
+    kc = rng.integers(-127, 128, size=(B, Hkv, Nk, D)).astype(np.int8)
+    mag = rng.integers(0, 0x7F, size=(B, Hkv, Nk, D))           # 0x7F (NaN) excluded
+    vc = (mag | (rng.integers(0, 2, size=mag.shape) << 7)).astype(np.uint8)
+    # power-of-two block scales keep every dequantised value exact in fp32
+    ks = np.ldexp(1.0, rng.integers(-9, -4, size=(B, Hkv, nblk))).astype(np.float32)
+    vs = np.ldexp(1.0, rng.integers(-6, 0, size=(B, Hkv, nblk))).astype(np.float32)
+    return kc, ks, vc, vs
+
+
+def _per_key(scales, Nk):
+    return np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :Nk, None]
+
+
+@pytest.mark.parametrize("causal,window_lo,pos0", [(False, 0, 0), (True, 0, 147), (True, 40, 100),
+                                                    (False, 130, 0)])
+def test_kvq_exact_cache_matches_attention(causal, window_lo, pos0):
+    # codes * power-of-two scales are exact fp32 values: attention over the cache
+    # must equal exact attention over those values (V decoded by torch's cast)
+    B, Hq, Hkv, Nq, Nk, D = 2, 6, 3, 3, 150, 64
+    rng = np.random.default_rng(5)
+    kc, ks, vc, vs = _random_cache(rng, B, Hkv, Nk, D)
+    kf = torch.from_numpy((kc.astype(np.float64) * _per_key(ks, Nk)).astype(np.float32))
+    vf = torch.from_numpy((_f8_values(vc) * _per_key(vs, Nk)).astype(np.float32))
+    q = normal((B, Hq, Nq, D), 11, torch.float32)
+    sc = 0.125
+    want = oracle.attn(q, kf, vf, scale=sc, causal=causal, window_lo=window_lo, pos0=pos0)
+    got = oracle.attn_kvq(q, kc, ks, vc, vs, scale=sc, causal=causal, window_lo=window_lo,
+                          pos0=pos0)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_kvq_zero_keys_give_the_mean_of_visible_values():
+    # all K codes 0: every score is 0, so each row is the plain mean of the
+    # values of its visible keys
+    B, Hq, Hkv, Nq, Nk, D = 1, 4, 2, 5, 200, 64
+    rng = np.random.default_rng(9)
+    _, ks, vc, vs = _random_cache(rng, B, Hkv, Nk, D)
+    kc = np.zeros((B, Hkv, Nk, D), dtype=np.int8)
+    q = normal((B, Hq, Nq, D), 3, torch.float16)
+    vals = _f8_values(vc) * _per_key(vs, Nk)
+    pos0, wlo = 150, 20
+    got = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.3, causal=True, window_lo=wlo, pos0=pos0)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        for i in range(Nq):
+            want = vals[0, g, wlo:pos0 + i + 1].mean(axis=0)
+            np.testing.assert_allclose(got[0, h, i], want, rtol=1e-12, atol=1e-15)
+
+
+def test_kvq_quantised_q_on_the_grid_is_exact():
+    # Q entries on the INT8 grid of its own block (integer codes times 2^-5,
+    # with a 127 in every head's block): scale 2^-5 and inverse 2^5 are exact,
+    # so the quantised Q reproduces Q and both variants agree bit for bit
+    B, Hq, Hkv, Nq, Nk, D = 1, 4, 2, 3, 130, 128
+    rng = np.random.default_rng(4)
+    kc, ks, vc, vs = _random_cache(rng, B, Hkv, Nk, D)
+    qi = rng.integers(-126, 127, size=(B, Hq, Nq, D)).astype(np.float32)
+    qi[:, :, 0, 0] = 127.0
+    q = torch.from_numpy(np.ldexp(qi, -5).astype(np.float32))
+    a = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.09, quant_q=False)
+    b = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.09, quant_q=True)
+    assert np.array_equal(a, b)
+
+
+def test_kvq_quantised_q_uses_per_head_blocks():
+    # off the grid, quant_q uses the dequantised per-(head, 64-row block) codes:
+    # the same as passing those values in as Q (70 rows: two blocks per head)
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 1, 70, 100, 64
+    rng = np.random.default_rng(8)
+    kc, ks, vc, vs = _random_cache(rng, B, Hkv, Nk, D)
+    q = normal((B, Hq, Nq, D), 21, torch.bfloat16)
+    qc, qs = oracle.quant_int8(q)
+    qd = torch.from_numpy((qc.astype(np.float64) *
+                           np.repeat(qs.astype(np.float64), 64, axis=2)[:, :, :Nq, None])
+                          .astype(np.float32))
+    a = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.125, quant_q=True)
+    b = oracle.attn_kvq(qd, kc, ks, vc, vs, scale=0.125, quant_q=False)
+    # (Q's dequantised values are rounded to fp32 for the second call)
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-5)
+    c = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.125, quant_q=False)
+    assert np.abs(a - c).max() > 1e-3   # the quantisation is really applied
