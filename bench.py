@@ -105,22 +105,36 @@ def bench_quant_prep(w, iters=5):
 
 def bench_decode(w, nbuf=48, reps=20):
     """Cold-cache decode: nbuf independent KV caches, one call per cache, captured
-    in a HIP graph; returns (us per call cold, us per call hot, bytes per call)."""
+    in a HIP graph; returns (us per call cold, us per call hot, bytes per call).
+    w.mode 2: the cache is INT8 K / E4M3 V codes with per-64-key scales."""
     import torch
     import scaled_dot_product_amd as sdpa
-    from scaled_dot_product_amd.inputs import make_qkv
+    from scaled_dot_product_amd.inputs import SEED_Q, make_kv_codes, make_qkv, normal
     dev = torch.device("cuda:0")
-    q0, k0, v0 = (t.to(dev) for t in make_qkv(w))
+    kvq = w.mode == 2
+    if kvq:
+        q0 = normal(w.q_shape, SEED_Q, w.dtype).to(dev)
+        kv0 = [t.to(dev) for t in make_kv_codes(w)]
+        ws_n = sdpa.decode_kvq_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
+                                               causal=w.causal, window_lo=w.window_lo,
+                                               pos0=w.pos0, dtype=w.dtype)
+    else:
+        q0, k0, v0 = (t.to(dev) for t in make_qkv(w))
+        kv0 = [k0, v0]
+        ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                        window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype)
     # nbuf copies at distinct addresses: together larger than every cache level
-    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nbuf)]
-    ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
-                                    window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype)
+    sets = [(q0.clone(), [t.clone() for t in kv0], torch.empty_like(q0)) for _ in range(nbuf)]
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def call(i):
-        q, k, v, o = sets[i]
-        sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, scale=w.scale,
-                 out=o, workspace=ws)
+        q, kv, o = sets[i]
+        if kvq:
+            sdpa.decode_kvq(q, *kv, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                            scale=w.scale, out=o, workspace=ws)
+        else:
+            sdpa.fwd(q, *kv, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                     scale=w.scale, out=o, workspace=ws)
 
     for i in range(nbuf):
         call(i)
@@ -150,11 +164,21 @@ def bench_decode(w, nbuf=48, reps=20):
         torch.cuda.synchronize()
         results[label] = e0.elapsed_time(e1) * 1e3 / (reps * len(order))
         del g
-    # algorithmic bytes: K and V rows of the visible keys, Q in, O out
+    return results["cold"], results["hot"], decode_bytes(w)
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode call: K and V rows of the visible keys (2
+    bytes per element, or 1 per code plus one fp32 scale per 64-key block and
+    tensor for a quantised cache), Q in, O out."""
     lo = w.window_lo
     hi = min(w.Nk, w.pos0 + w.Nq) if w.causal else w.Nk
-    nbytes = 2 * w.B * w.Hkv * (hi - lo) * w.D * 2 + 2 * w.B * w.Hq * w.Nq * w.D * 2
-    return results["cold"], results["hot"], nbytes
+    if w.mode == 2:
+        tiles = (hi + 63) // 64 - lo // 64 if hi > lo else 0
+        kv = 2 * w.B * w.Hkv * ((hi - lo) * w.D + tiles * 4)
+    else:
+        kv = 2 * w.B * w.Hkv * (hi - lo) * w.D * 2
+    return kv + 2 * w.B * w.Hq * w.Nq * w.D * 2
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -243,6 +267,24 @@ def run_extra(part):
                               "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1)}
             log(f"decode sweep Nk={nk}: {cold_us:.2f} us, {sweep[str(nk)]['gbs_cold']} GB/s")
         extra["decode_kv_sweep"] = sweep
+    elif part == "decode_kvq":
+        wk = WORKLOADS["gqa_decode_kvq_f16_4096"]
+        cold_us, hot_us, nbytes = bench_decode(wk)
+        extra["decode_kvq"] = {"workload": wk.name, "us_per_call_cold": round(cold_us, 3),
+                               "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
+                               "us_per_call_hot": round(hot_us, 3), "bytes_per_call": nbytes,
+                               "frac_of_hbm_peak_cold": round(nbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"decode_kvq: cold {cold_us:.2f} us ({extra['decode_kvq']['gbs_cold']} GB/s), hot {hot_us:.2f} us")
+        sweep = {}
+        for nk in (4096, 8192, 16384, 32768, 65536):
+            wd = wk.variant(Nk=nk, pos0=nk - 4)
+            per = 2 * wd.B * wd.Hkv * nk * wd.D
+            nbuf = max(3, min(48, -(-640_000_000 // per)))   # > 600 MB of caches: cold
+            cold_us, _, nbytes = bench_decode(wd, nbuf=nbuf, reps=10)
+            sweep[str(nk)] = {"us_cold": round(cold_us, 2),
+                              "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1)}
+            log(f"decode_kvq sweep Nk={nk}: {cold_us:.2f} us, {sweep[str(nk)]['gbs_cold']} GB/s")
+        extra["decode_kvq_kv_sweep"] = sweep
     return extra
 
 
@@ -297,7 +339,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "quant", "causal", "sdxl", "copy"],
+    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "causal", "sdxl", "copy"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -331,7 +373,7 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "causal", "sdxl", "decode"):
+        for part in ("quant", "causal", "sdxl", "decode", "decode_kvq"):
             extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)

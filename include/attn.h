@@ -136,6 +136,46 @@ int attn_quantize_qk(const void* q, const void* k, int8_t* q_codes, float* q_sca
 int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales,
                     int B, int Hkv, int Nk, int D, int dtype, void* stream);
 
+/*
+ * attn_decode_kvq — decode over a quantised KV cache: the split-KV decode of
+ * attn_fwd reading K and V as the per-block codes that attn_quantize_qk (its
+ * K half) and attn_quantize_v write, at half the bytes of a 16-bit cache.
+ * This is the "INT8 QK . FP8 PV" recipe of the table in section 1 of
+ * "Attention kernels on a home RTX 5080" applied to the cache; the pages'
+ * own kernels quantise a 16-bit cache on every call instead.
+ *
+ *   q          device [B][Hq][Nq][D], f16 or bf16 (`dtype`).
+ *   k_codes    device int8 [B][Hkv][Nk][D]; key j of a head dequantises to
+ *              k_codes * k_scales[b][h][j / 64].
+ *   k_scales   device fp32 [B][Hkv][ceil(Nk/64)].
+ *   v_codes    device uint8 [B][Hkv][Nk][D], OCP FP8 E4M3 codes; value
+ *              E4M3(code) * v_scales[b][h][j / 64].
+ *   v_scales   device fp32 [B][Hkv][ceil(Nk/64)].
+ *   o          device [B][Hq][Nq][D], `dtype`.
+ *   B .. scale, stream: as for attn_fwd. (Hq / Hkv) * Nq must be <= 32 (all
+ *              query rows of a key/value head fit one 32-column matrix-core
+ *              block) and B * Hkv <= 65535; otherwise ATTN_E_UNSUPPORTED.
+ *   workspace  device scratch of at least attn_decode_kvq_workspace_bytes(...)
+ *              bytes, 256-byte aligned, no initialisation needed.
+ *
+ * In the kernel, Q is quantised with the INT8 recipe of attn_quantize_qk (the
+ * Nq <= 32 rows of one head are one block), Q K^T is computed exactly in
+ * int32 and scaled by the block scales, and each softmax weight enters P V as
+ * an E4M3 code (fp32 accumulation; the denominator sums the unrounded
+ * weights). Scales may be 0 (a block of zero codes); codes 0x7F/0xFF (NaN)
+ * give NaN outputs. A row with no visible key is written as zeros. Returns
+ * ATTN_OK or a negative attn_status; nothing is enqueued on error.
+ */
+int attn_decode_kvq(const void* q, const int8_t* k_codes, const float* k_scales,
+                    const uint8_t* v_codes, const float* v_scales, void* o,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                    int causal, int window_lo, int pos0, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace attn_decode_kvq needs (host-only; 0 for arguments it rejects). */
+size_t attn_decode_kvq_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                       int causal, int window_lo, int pos0, int dtype);
+
 /* Static English text for a status code. */
 const char* attn_status_string(int status);
 

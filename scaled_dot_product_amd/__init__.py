@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_workspace_bytes", "quantize_qk", "quantize_v", "load_library",
+__all__ = ["fwd", "fwd_workspace_bytes", "quantize_qk", "quantize_v", "decode_kvq",
+           "decode_kvq_workspace_bytes", "load_library",
            "MODE_EXACT", "MODE_QUANT", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -48,6 +49,11 @@ def load_library():
     lib.attn_quantize_qk.restype = i
     lib.attn_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     lib.attn_quantize_v.restype = i
+    lib.attn_decode_kvq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
+                                     vp, sz, vp]
+    lib.attn_decode_kvq.restype = i
+    lib.attn_decode_kvq_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i]
+    lib.attn_decode_kvq_workspace_bytes.restype = sz
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -146,3 +152,57 @@ def quantize_v(v: torch.Tensor):
                              _DTYPE.get(v.dtype, -1), _stream_handle(v))
     _check(st, "attn_quantize_v")
     return vc, vs
+
+
+def decode_kvq_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos0=0,
+                               dtype=torch.float16) -> int:
+    return int(load_library().attn_decode_kvq_workspace_bytes(
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), _DTYPE[dtype]))
+
+
+def decode_kvq(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+               v_codes: torch.Tensor, v_scales: torch.Tensor, *, causal=False, window_lo=0,
+               pos0=0, scale=None, out=None, workspace=None) -> torch.Tensor:
+    """Decode over a quantised KV cache on the current stream.
+
+    q: [B, Hq, Nq, D] f16/bf16; k_codes int8 and v_codes uint8 (E4M3) [B, Hkv, Nk, D];
+    k_scales, v_scales fp32 [B, Hkv, ceil(Nk/64)] (the outputs of quantize_qk's K half
+    and quantize_v). (Hq / Hkv) * Nq must be <= 32. Returns O [B, Hq, Nq, D] in q's dtype.
+    """
+    lib = load_library()
+    for t, name in ((q, "q"), (k_codes, "k_codes"), (k_scales, "k_scales"),
+                    (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, name)
+    if q.dim() != 4 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape:
+        raise AttnError("expected q [B,Hq,Nq,D] and k_codes, v_codes [B,Hkv,Nk,D]")
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.uint8:
+        raise AttnError("k_codes must be int8 and v_codes uint8")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, Dk = k_codes.shape
+    if Dk != D or k_codes.shape[0] != B:
+        raise AttnError("q and the codes disagree on B or D")
+    sshape = (B, Hkv, (Nk + 63) // 64)
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or tuple(t.shape) != sshape:
+            raise AttnError(f"{name} must be float32 of shape {sshape}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise AttnError("out must match q's shape and dtype")
+    dt = _DTYPE.get(q.dtype, -1)
+    need = int(lib.attn_decode_kvq_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
+                                                   int(window_lo), int(pos0), dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.attn_decode_kvq(q.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(),
+                             v_codes.data_ptr(), v_scales.data_ptr(), out.data_ptr(),
+                             B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo),
+                             int(pos0), float(scale), dt, ws_ptr, ws_len, _stream_handle(q))
+    _check(st, "attn_decode_kvq")
+    return out

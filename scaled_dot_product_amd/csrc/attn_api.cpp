@@ -44,6 +44,20 @@ int check_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int win
   return ATTN_OK;
 }
 
+// The quantised-cache decode packs the G * Nq query rows of a key/value head
+// into one 32-column MFMA block and launches one grid row per key/value head.
+int check_kvq(int B, int Hq, int Hkv, int Nq, int Nk, int D, int window_lo, int pos0,
+              float scale, int dtype) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (window_lo < 0 || pos0 < 0) return ATTN_E_INVALID;
+  if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_E_INVALID;
+  if ((int64_t)(Hq / Hkv) * Nq > 32) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * Hkv > 65535) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 int elem_size(int dtype) { return dtype == ATTN_DT_F32 ? 4 : 2; }
 
 FwdArgs make_args(const void* q, const void* k, const void* v, void* o, int B, int Hq,
@@ -198,12 +212,42 @@ int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales, int B, int
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+size_t attn_decode_kvq_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                       int causal, int window_lo, int pos0, int dtype) {
+  if (check_kvq(B, Hq, Hkv, Nq, Nk, D, window_lo, pos0, 1.0f, dtype) != ATTN_OK) return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  return round_up(decode_plan(a).ws_bytes);
+}
+
+int attn_decode_kvq(const void* q, const int8_t* k_codes, const float* k_scales,
+                    const uint8_t* v_codes, const float* v_scales, void* o, int B, int Hq,
+                    int Hkv, int Nq, int Nk, int D, int causal, int window_lo, int pos0,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int st = check_kvq(B, Hq, Hkv, Nq, Nk, D, window_lo, pos0, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o) ||
+      ((uintptr_t)k_scales & 3u) || ((uintptr_t)v_scales & 3u))
+    return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, nullptr, nullptr, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo,
+                        pos0, scale);
+  const DecodePlan plan = decode_plan(a);
+  if (workspace_bytes < round_up(plan.ws_bytes)) return ATTN_E_WORKSPACE;
+  if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) != 0) return ATTN_E_INVALID;
+  const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+  const hipError_t e = launch_decode_kvq(a, plan, k_codes, k_scales, v_codes, v_scales, elem,
+                                         workspace, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_INVALID: return "invalid argument (null or misaligned pointer, bad size, position, window or scale)";
-    case ATTN_E_UNSUPPORTED: return "unsupported head dimension, dtype or mode";
-    case ATTN_E_WORKSPACE: return "workspace smaller than attn_fwd_workspace_bytes()";
+    case ATTN_E_UNSUPPORTED: return "unsupported head dimension, dtype, mode or shape";
+    case ATTN_E_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() result";
     case ATTN_E_HIP: return "the HIP runtime refused a kernel launch";
     default: return "unknown status";
   }

@@ -24,6 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -100,6 +101,42 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
 #endif
 }
 
+// gfx950 LDS transpose read of bytes (ds_read_b64_tr_b8). Within each
+// 16-lane group, lane 8h + c receives as its byte k (k = 0..7) byte c of the
+// 8 bytes whose address lane h + 2k supplies.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p));
+#else
+  (void)p;
+  return u32x2{0, 0};
+#endif
+}
+
+// 16-bit element bits -> float (exact widening).
+template <typename T>
+__device__ __forceinline__ float elem_to_float(uint32_t bits16);
+template <>
+__device__ __forceinline__ float elem_to_float<__bf16>(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+template <>
+__device__ __forceinline__ float elem_to_float<_Float16>(uint32_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
+  return (float)h;
+}
+
+// Unpack one 16-byte chunk (8 elements) to floats.
+template <typename T>
+__device__ __forceinline__ void unpack8(u32x4 raw, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = elem_to_float<T>(raw[i] & 0xffffu);
+    x[2 * i + 1] = elem_to_float<T>(raw[i] >> 16);
+  }
+}
+
 // Direct global -> LDS load of 16 bytes per lane: lane i's 16 bytes, read
 // from base + off_i, land at lds_base + 16 i (base and lds_base must be the
 // same for the whole wave; M0 carries the LDS address). Written as inline asm
@@ -122,6 +159,10 @@ __device__ __forceinline__ void load_to_lds16(const void* base, uint32_t off, vo
 // including global -> LDS loads (s_waitcnt vmcnt(0); the other counters are
 // left alone).
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt immediate that waits until at most n (< 64) vector-memory
+// operations of this wave are outstanding (they complete in issue order).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Workgroup id -> logical tile so that tiles [x*T/8, (x+1)*T/8) run on XCD x
 // (the dispatcher places workgroup w on XCD w % 8); neighbouring tiles, which

@@ -411,6 +411,342 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   decode_finish<TO, D, kWaves>(a, p, m, l, oacc, (float*)sk_all, sml, ctr_seen);
 }
 
+// Decode over a quantised KV cache: K as INT8 codes and V as FP8 E4M3 codes,
+// each with one fp32 scale per 64-key block of a key/value head (what
+// attn_quantize_qk and attn_quantize_v write). This is the "INT8 QK . FP8 PV"
+// recipe of the table in section 1 of "Attention kernels on a home RTX 5080"
+// applied to the cache, which halves the bytes decode streams. Same split,
+// tiles and merge as decode_kernel; per tile:
+//   S_int^T = Kc Qc^T             i8 MFMA 32x32x32, exact int32 (Q is
+//                                 quantised here with the same per-block
+//                                 recipe: a head's Nq <= 32 rows are one block)
+//   z = S_int * s_q * s_k * scale * log2(e)     (log2 units)
+//   P^ = E4M3(448 * 2^-(margin + 3) * 2^(z - m) * s_v / s_ref)
+//   O_acc += Vc^T P^T              fp8 MFMA 32x32x64, fp32 accumulation
+//   l += sum of 2^(z - m) (unquantised)
+// m is a running maximum allowed to trail the scores by up to 2 (log2 units)
+// and s_ref a reference V block scale allowed to trail the wave's largest by
+// up to a factor 2; only when either is exceeded are they raised and O_acc
+// and l rescaled. So every weight stays <= 448, and
+// O = O_acc * s_ref * 2^(margin + 3) / 448 / l.
+template <typename TO, int D, int kWaves>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves)))
+decode_kvq_kernel(FwdArgs a, DecodeArgs p, const int8_t* __restrict__ kc,
+                  const float* __restrict__ ks, const uint8_t* __restrict__ vc,
+                  const float* __restrict__ vs) {
+  constexpr int KS = D / 32;            // i8 k-steps of 32 channels
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 16;           // 16-byte chunks per code row
+  constexpr int RPI = 64 / CPR;         // code rows one 64-lane direct load covers
+  constexpr int NL = 64 / RPI;          // direct loads per 64-row code tile
+  constexpr int TILEB = 64 * D;         // bytes of one K or V code tile
+  constexpr int CQ = D / 8;             // 16-byte chunks per 16-bit Q row
+  constexpr int NQI = 32 * CQ / 64;     // direct loads for 32 Q rows
+  static_assert(NQI % kWaves == 0, "Q rows split evenly over the waves");
+  constexpr float kLog2_448 = 8.807354922057604f;
+  // exp2 rounds within an ulp or so; lowering the weights by 2^-12 keeps every
+  // one <= 448 (the largest E4M3 magnitude) without a clamp
+  constexpr float kMargin = 2.44140625e-4f;
+  constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
+  // lags (log2 units) of the running maximum and of the V-scale reference
+  // before O is rescaled; the weights' FP8 scale is lowered by 2^(kLag + kLagV)
+  constexpr float kLag = 2.0f, kLagV = 1.0f;
+  // Per wave two K and two V code tiles (the tile in hand and the next one
+  // stay in flight together); the cross-wave merge reuses the first half of
+  // them (32 x D floats per wave). Q comes in through a staging area of its own.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * 4 * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t sqst[32 * D * 2];
+  __shared__ float sml[2 * kWaves * 32];
+  static_assert(2 * TILEB == 32 * D * (int)sizeof(float), "merge area must fit the tiles");
+  static_assert(4 * NL < 64, "outstanding loads must fit the vmcnt counter");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int split = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int nkt = (a.Nk + 63) / 64;
+  const int8_t* Kc = kc + (int64_t)bg * a.Nk * D;
+  const uint8_t* Vc = vc + (int64_t)bg * a.Nk * D;
+  const float* Ks = ks + (int64_t)bg * nkt;
+  const float* Vs = vs + (int64_t)bg * nkt;
+  // slot s of this wave: K tile at sk + 2 s TILEB, V tile TILEB above it
+  uint8_t* sk = lds + wave * 4 * TILEB;
+
+  // The G * Nq query rows of this key/value head are contiguous in Q (heads
+  // g G .. g G + G - 1): column n = hh * Nq + i is row n of that block. They
+  // come into LDS by direct loads (rows past the packed ones repeat the last),
+  // chunk c of row n at position c ^ qswz(n).
+  auto qswz = [](int n) { return CQ == 16 ? (n & 15) : ((n >> 1) & 7); };
+  {
+    const char* qbase = (const char*)((const TO*)a.q + ((int64_t)b * a.Hq + g * G) * a.Nq * D);
+#pragma unroll
+    for (int u0 = 0; u0 < NQI / kWaves; ++u0) {
+      const int u = u0 * kWaves + wave;
+      const int n = (64 * u + lane) / CQ, pos = lane % CQ;
+      load_to_lds16(qbase, (uint32_t)((min(n, p.rows - 1) * D + 8 * (pos ^ qswz(n))) * 2),
+                    sqst + 1024 * u);
+    }
+  }
+
+  // K code row r holds key 32 h + 16 blk + 4 a + c for r = 32 blk + 8 a + 4 h + c
+  // (lane half h's 32 scores are keys 32 h .. 32 h + 31 in B-operand order); V
+  // code rows are keys in order. Chunk c of a row sits at c ^ kswz(r) or
+  // c ^ vswz(r): the operand reads of a 16- or 32-lane group hit distinct
+  // banks. Rows past Nk clamp to the last key (masked).
+  auto kswz = [](int r) { return CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  auto vswz = [](int r) { return CPR == 8 ? (r & 7) : 2 * ((r >> 2) & 1); };
+  auto load_k = [&](int t, int slot) {
+    const int8_t* base = Kc + (int64_t)64 * t * D;
+    uint8_t* dst = sk + 2 * TILEB * slot;
+    const int last = a.Nk - 1 - 64 * t;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r = RPI * u + lane / CPR, pos = lane % CPR;
+      const int key = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+      load_to_lds16(base, (uint32_t)(min(key, last) * D + 16 * (pos ^ kswz(r))), dst + RPI * u * D);
+    }
+  };
+  auto load_v = [&](int t, int slot) {
+    const uint8_t* base = Vc + (int64_t)64 * t * D;
+    uint8_t* dst = sk + 2 * TILEB * slot + TILEB;
+    const int last = a.Nk - 1 - 64 * t;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r = RPI * u + lane / CPR, pos = lane % CPR;
+      load_to_lds16(base, (uint32_t)(min(r, last) * D + 16 * (pos ^ vswz(r))), dst + RPI * u * D);
+    }
+  };
+
+  const int t0 = p.t_lo + split * p.tiles_per_wg;
+  const int t1 = min(t0 + p.tiles_per_wg, p.t_hi);
+  int t = t0 + wave;
+  float kst = 0.0f, vst = 0.0f;   // block scales of the tile in hand
+  // this wave's first two tiles go in flight behind its Q loads, which must
+  // land first (loads complete in issue order)
+  if (t + kWaves < t1) {
+    load_k(t, 0);
+    load_v(t, 0);
+    load_k(t + kWaves, 1);
+    load_v(t + kWaves, 1);
+    kst = Ks[t];
+    vst = Vs[t];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NL));
+  } else if (t < t1) {
+    load_k(t, 0);
+    load_v(t, 0);
+    kst = Ks[t];
+    vst = Vs[t];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NL));
+  } else {
+    vmem_wait_all();
+  }
+  __syncthreads();   // every wave's share of Q is in LDS
+
+  // Q codes while the first tiles are in flight. Lane (col, half) holds, for
+  // k-step k, channels 32 k + 16 half + (0..15) of row col (B-operand order).
+  const bool cvalid = col < p.rows;
+  const int ccol = cvalid ? col : 0;
+  const int hh = ccol / a.Nq, qi = ccol - hh * a.Nq;
+  float x[KS][16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = 4 * k + 2 * half + c;
+      unpack8<TO>(*(const u32x4*)&sqst[(ccol * CQ + (ch ^ qswz(ccol))) * 16], &x[k][8 * c]);
+    }
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[k][i]));
+  amax = halves_max(amax);
+  float hmax = 0.0f;   // over the Nq rows of query head hh
+  for (int j = 0; j < a.Nq; ++j) hmax = fmaxf(hmax, __shfl(amax, hh * a.Nq + j, 64));
+  // fp32, correctly rounded: the block recipe of the INT8 quantiser
+  const float sq = hmax > 0.0f ? hmax / 127.0f : 0.0f;
+  const float qinv = hmax > 0.0f ? 127.0f / hmax : 0.0f;
+  i32x4 qv[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float r = __builtin_rintf(x[k][4 * w4 + i] * qinv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+      }
+      qv[k][w4] = (int)w;
+    }
+  const float cfq = sq * a.c;
+
+  unsigned long long ctr_seen = 0;
+  if (tid == 0) ctr_seen = __hip_atomic_load(p.ctr + bg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  float lref = -INFINITY;   // log2 of the largest V block scale seen so far
+
+  // The int32 scores start from 0x4B400000, the bit pattern of 1.5 * 2^23:
+  // |S| < 2^22, so each accumulator read as a float is exactly 1.5 * 2^23 + S.
+  i32x16 magic;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) magic[j] = 0x4B400000;
+  asm volatile("" : "+v"(magic));
+
+  auto tile = [&](int t, int slot) {
+    const int k0 = t * 64;
+    const bool next = t + kWaves < t1;       // loads in flight behind this tile's
+    const bool more = t + 2 * kWaves < t1;   // a tile to load into this slot
+    const float kst_c = kst, vst_c = vst;
+    if (next) {
+      // uniform index: scalar loads, which do not wait behind the tile loads
+      const int tn = __builtin_amdgcn_readfirstlane(t + kWaves);
+      kst = Ks[tn];
+      vst = Vs[tn];
+    }
+    // this tile's code tiles have landed (untracked loads; only the next
+    // tile's may still be in flight)
+    if (next)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NL));
+    else
+      vmem_wait_all();
+    const uint8_t* tk = sk + 2 * TILEB * slot;
+    const uint8_t* tv = tk + TILEB;
+    i32x16 s[2];
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + col;
+        const i32x4 ka = *(const i32x4*)&tk[r * D + 16 * ((2 * k + half) ^ kswz(r))];
+        s[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv[k], k == 0 ? magic : s[mb], 0, 0, 0);
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): K reads returned
+    if (more) load_k(t + 2 * kWaves, slot);
+
+    // A block of zero codes has scale 0; the floor keeps masked scores at
+    // -inf (-inf * 0 would be NaN) and changes nothing else.
+    const float cf = fmaxf(cfq * kst_c, 1.17549435e-38f);
+    float sf[2][16];   // kOff + S, exact
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sf[mb][j] = __builtin_bit_cast(f32x16, s[mb])[j];
+    // Only tiles that straddle a bound are masked (columns past the packed
+    // rows compute finite values that are never published).
+    if (k0 < a.window_lo || k0 + 64 > a.Nk || (a.causal && k0 + 63 > a.pos0)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * half + 16 * mb + 4 * (j >> 2) + (j & 3);
+          const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
+                           (!a.causal || key <= a.pos0 + qi);
+          if (!vis) sf[mb][j] = -INFINITY;
+        }
+    }
+    float mx = sf[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sf[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sf[1][j]);
+    mx = (halves_max(mx) - kOff) * cf;   // exact subtraction
+    const float lv = __builtin_amdgcn_logf(fmaxf(vst_c, 1.17549435e-38f));
+    // O and l are rescaled only when a column's maximum runs more than kLag
+    // ahead of m, or the V scale more than kLagV ahead of the reference; the
+    // weights' FP8 scale leaves room for both, so none exceeds 448 meanwhile.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLag) || lv > lref + kLagV) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      const float lref_new = fmaxf(lref, lv);
+      const float ab = alpha * __builtin_amdgcn_exp2f(lref - lref_new);   // 0 before any tile
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= ab;
+      m = m_new;
+      lref = lref_new;
+    }
+    const float bias = (lv - lref) + (kLog2_448 - kMargin - kLag - kLagV);
+    const float mu = (m == -INFINITY ? 0.0f : m) - bias;
+    // exponent = S cf - mu = (kOff + S) cf - (kOff cf + mu): one FMA per score.
+    // Rounding kOff cf + mu moves every exponent of the tile by at most
+    // 2^-24 |kOff cf + mu| < 0.9 cf + 2^-21, far below the INT8 rounding of
+    // the scores and within the headroom to the E4M3 rounding boundary 464 for
+    // cf < 0.03; larger factors take the exact form.
+    float C = fmaf(kOff, cf, mu);
+    if (cf >= 0.03f) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sf[mb][j] -= kOff;
+      C = mu;
+    }
+    i32x8 pb;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -C));
+          ls[k] += e[k];
+        }
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
+        pb[4 * mb + q4] = pk;
+      }
+    // the denominator takes the weights back to their unscaled values
+    l += halves_sum((ls[0] + ls[1]) + (ls[2] + ls[3])) * __builtin_amdgcn_exp2f(-bias);
+
+    // O^T += V^T P^T: lane 16 g + tt of a transpose read names key
+    // 32 (g / 2) + 8 q + tt / 2 at channels 32 db + 16 (g % 2) + 8 (tt % 2) + (0..7);
+    // four reads give lane (col, half) channel 32 db + col of keys 32 half + (0..31).
+    const int gq = lane >> 4, tt = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c16 = 2 * db + (gq & 1);
+      i32x8 va;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int key = 32 * (gq >> 1) + 8 * q + (tt >> 1);
+        const u32x2 w = lds_read_tr8(&tv[key * D + 16 * (c16 ^ vswz(key)) + 8 * (tt & 1)]);
+        va[2 * q] = (int)w[0];
+        va[2 * q + 1] = (int)w[1];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): V reads returned
+      load_v(t + 2 * kWaves, slot);
+    }
+  };
+  for (int i = 0; t < t1; t += kWaves, ++i) tile(t, __builtin_amdgcn_readfirstlane(i & 1));
+
+  // back to V units: O_acc * s_ref * 2^(margin + lags) / 448
+  const float fac = lref == -INFINITY
+                        ? 0.0f
+                        : __builtin_amdgcn_exp2f(lref + (kMargin + kLag + kLagV)) * (1.0f / 448.0f);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[db][j] *= fac;
+  decode_finish<TO, D, kWaves>(a, p, m, l, oacc, (float*)lds, sml, ctr_seen);
+}
+
 // A different generation for every launch, from a per-process random start
 // (so that counters left in a reused workspace by another process never match).
 unsigned long long next_generation() {
@@ -421,8 +757,7 @@ unsigned long long next_generation() {
   return (g % ((1ull << 40) - 1)) + 1;
 }
 
-template <typename T, typename TO, int D>
-hipError_t launch_t(const FwdArgs& a, const DecodePlan& pl, void* ws, hipStream_t s) {
+DecodeArgs decode_args(const FwdArgs& a, const DecodePlan& pl, void* ws) {
   DecodeArgs p;
   p.rows = pl.rows;
   p.t_lo = pl.t_lo;
@@ -432,9 +767,15 @@ hipError_t launch_t(const FwdArgs& a, const DecodePlan& pl, void* ws, hipStream_
   const int64_t nrow = (int64_t)a.B * a.Hkv * pl.nsplit * pl.rows;
   p.ctr = (unsigned long long*)ws;
   p.opart = (float*)((char*)ws + pl.ctr_bytes);
-  p.mpart = p.opart + nrow * D;
+  p.mpart = p.opart + nrow * a.D;
   p.lpart = p.mpart + nrow;
   p.gen = next_generation();
+  return p;
+}
+
+template <typename T, typename TO, int D>
+hipError_t launch_t(const FwdArgs& a, const DecodePlan& pl, void* ws, hipStream_t s) {
+  const DecodeArgs p = decode_args(a, pl, ws);
   const dim3 grid(pl.nsplit, a.B * a.Hkv);
   if (pl.waves == 1)
     hipLaunchKernelGGL((decode_kernel<T, TO, D, 1>), grid, dim3(64), 0, s, a, p);
@@ -442,6 +783,17 @@ hipError_t launch_t(const FwdArgs& a, const DecodePlan& pl, void* ws, hipStream_
     hipLaunchKernelGGL((decode_kernel<T, TO, D, 2>), grid, dim3(128), 0, s, a, p);
   else
     hipLaunchKernelGGL((decode_kernel<T, TO, D, 4>), grid, dim3(256), 0, s, a, p);
+  return hipGetLastError();
+}
+
+template <typename TO, int D>
+hipError_t launch_kvq_t(const FwdArgs& a, const DecodePlan& pl, const int8_t* kc,
+                        const float* ks, const uint8_t* vc, const float* vs, void* ws,
+                        hipStream_t s) {
+  if (pl.waves != 4) return hipErrorInvalidConfiguration;
+  const DecodeArgs p = decode_args(a, pl, ws);
+  const dim3 grid(pl.nsplit, a.B * a.Hkv);
+  hipLaunchKernelGGL((decode_kvq_kernel<TO, D, 4>), grid, dim3(256), 0, s, a, p, kc, ks, vc, vs);
   return hipGetLastError();
 }
 
@@ -485,6 +837,16 @@ hipError_t launch_decode(const FwdArgs& a, const DecodePlan& p, int elem, bool o
     return a.D == 64 ? launch_t<__bf16, __bf16, 64>(a, p, ws, s) : launch_t<__bf16, __bf16, 128>(a, p, ws, s);
   }
   return a.D == 64 ? launch_t<_Float16, _Float16, 64>(a, p, ws, s) : launch_t<_Float16, _Float16, 128>(a, p, ws, s);
+}
+
+hipError_t launch_decode_kvq(const FwdArgs& a, const DecodePlan& p, const int8_t* kc,
+                             const float* ks, const uint8_t* vc, const float* vs, int elem,
+                             void* ws, hipStream_t s) {
+  if (elem == 2)
+    return a.D == 64 ? launch_kvq_t<__bf16, 64>(a, p, kc, ks, vc, vs, ws, s)
+                     : launch_kvq_t<__bf16, 128>(a, p, kc, ks, vc, vs, ws, s);
+  return a.D == 64 ? launch_kvq_t<_Float16, 64>(a, p, kc, ks, vc, vs, ws, s)
+                   : launch_kvq_t<_Float16, 128>(a, p, kc, ks, vc, vs, ws, s);
 }
 
 }  // namespace attn

@@ -48,6 +48,12 @@ DecodePlan decode_plan(const FwdArgs& a);
 hipError_t launch_decode(const FwdArgs& a, const DecodePlan& p, int elem, bool out_f32,
                          void* ws, hipStream_t s);
 
+// Decode over a quantised KV cache (INT8 K codes, E4M3 V codes, fp32 scales
+// per 64-key block) with the plan above; elem: 1 = f16, 2 = bf16 Q and O.
+hipError_t launch_decode_kvq(const FwdArgs& a, const DecodePlan& p, const int8_t* kc,
+                             const float* ks, const uint8_t* vc, const float* vs, int elem,
+                             void* ws, hipStream_t s);
+
 // ---- fp32 inputs: rounded to bf16 before the MFMA path --------------------
 hipError_t launch_f32_to_bf16(const float* x, void* y, int64_t n, hipStream_t s);
 

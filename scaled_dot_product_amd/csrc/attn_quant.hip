@@ -28,28 +28,6 @@ namespace attn {
 
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float elem_to_float(uint32_t bits16);
-template <>
-__device__ __forceinline__ float elem_to_float<__bf16>(uint32_t b) {
-  return __uint_as_float(b << 16);
-}
-template <>
-__device__ __forceinline__ float elem_to_float<_Float16>(uint32_t b) {
-  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
-  return (float)h;
-}
-
-// Unpack one 16-byte chunk (8 elements) to floats (exact widening).
-template <typename T>
-__device__ __forceinline__ void unpack8(u32x4 raw, float* x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = elem_to_float<T>(raw[i] & 0xffffu);
-    x[2 * i + 1] = elem_to_float<T>(raw[i] >> 16);
-  }
-}
-
 // Block amax over the workgroup (256 threads), identical in every thread.
 __device__ __forceinline__ float block_amax(float v, float* red) {
 #pragma unroll

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
-              "attn_quantize_v", "attn_status_string"):
+              "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
+              "attn_status_string"):
         assert n in names
 
 
@@ -119,3 +120,49 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(sdpa.AttnError):
         sdpa.fwd(q, q, q)
+
+
+def _kvq(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, o=FAKE, B=1, Hq=16, Hkv=8, Nq=4,
+             Nk=4096, D=128, causal=1, window_lo=0, pos0=4092, scale=0.088, dtype=1,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_kvq(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["o"], a["B"],
+                               a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["causal"],
+                               a["window_lo"], a["pos0"], a["scale"], a["dtype"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_INVALID),
+    (dict(kc=None), E_INVALID),
+    (dict(vs=None), E_INVALID),
+    (dict(o=None), E_INVALID),
+    (dict(vc=FAKE + 8), E_INVALID),            # codes need 16-byte alignment
+    (dict(ks=FAKE + 2), E_INVALID),            # scales need 4-byte alignment
+    (dict(ws=FAKE + 16), E_INVALID),           # workspace needs 256-byte alignment
+    (dict(ws=None), E_INVALID),
+    (dict(ws_bytes=64), E_WORKSPACE),
+    (dict(Hq=12, Hkv=8), E_INVALID),
+    (dict(Nk=0), E_INVALID),
+    (dict(window_lo=-1), E_INVALID),
+    (dict(scale=float("nan")), E_INVALID),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(dtype=0), E_UNSUPPORTED),            # fp32 Q is not supported here
+    (dict(Nq=17), E_UNSUPPORTED),              # 2 x 17 = 34 rows per KV head
+    (dict(B=8192, Hq=16, Hkv=16, Nq=1), E_UNSUPPORTED),   # more than 65535 KV heads
+])
+def test_decode_kvq_rejects_before_enqueue(lib, kw, want):
+    assert _kvq(lib, **kw) == want
+
+
+def test_decode_kvq_workspace_bytes(lib):
+    ws = lib.attn_decode_kvq_workspace_bytes
+    need = ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 1)
+    # arrival counters plus fp32 partials (O, max, sum) of every split and row
+    assert need >= 8 * 8 * (128 + 2) * 4
+    assert need % 256 == 0
+    assert ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0) == 0     # fp32 rejected
+    assert ws(1, 64, 1, 1, 4096, 128, 0, 0, 0, 2) == 0        # 64 rows per KV head
+    assert ws(1, 32, 1, 1, 4096, 64, 0, 0, 0, 2) > 0          # 32 rows fit
+    assert _kvq(lib, ws_bytes=need - 1) == E_WORKSPACE
