@@ -244,6 +244,7 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   constexpr int RPI = 64 / CPR;            // rows one 64-lane direct load covers
   constexpr int NL = 64 / RPI;             // direct loads per 64-row tile
   constexpr int TILE = 64 * D;             // elements of one K or V tile
+  constexpr float kLag = 2.0f;             // see the rescale below (log2 units)
   // Each wave streams its own tiles through a K and a V tile of its own in
   // LDS. The cross-wave merge reuses the K tiles' bytes (32 x D floats per
   // wave).
@@ -350,21 +351,39 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-        const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
-                         (!a.causal || key <= a.pos0 + qi);
-        sc[mb][j] = vis ? s[mb][0][j] + s[mb][1][j] : -INFINITY;
-      }
+      for (int j = 0; j < 16; ++j) sc[mb][j] = s[mb][0][j] + s[mb][1][j];
+    // Only tiles that straddle a bound are masked (columns past the packed
+    // rows compute finite values that are never published).
+    if (k0 < a.window_lo || k0 + 64 > a.Nk || (a.causal && k0 + 63 > a.pos0)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
+          const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
+                           (!a.causal || key <= a.pos0 + qi);
+          if (!vis) sc[mb][j] = -INFINITY;
+        }
+    }
     float mx = sc[0][0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[0][j]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[1][j]);
     mx = halves_max(mx) * a.c;
-    const float m_new = fmaxf(m, mx);
-    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
+    // O and l are rescaled only when a column's maximum runs more than kLag
+    // ahead of m; the weights meanwhile stay below 2^kLag.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLag)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m = m_new;
+    }
     const float mu = m == -INFINITY ? 0.0f : m;
     V8 pv[2][2];
     float lsum = 0.0f;
@@ -378,14 +397,12 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
           lsum += e;
           pv[mb][tt][i] = E::from_float(e);
         }
-    l = l * alpha + halves_sum(lsum);
+    l += halves_sum(lsum);
     // O^T += V^T P^T; the V^T operands come through transpose reads (as in the
     // prefill): lane r of a 16-lane group names key kb + r/4 at channel d0 + 4 (r % 4).
     const int gq = lane >> 4, rr = lane & 15;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
