@@ -56,7 +56,7 @@ def _load():
         lib = ctypes.CDLL(build())
         i, i64, d = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         vp = ctypes.c_void_p
-        lib.oracle_attn.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d,
+        lib.oracle_attn.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, d,
                                     vp, i64, vp, vp, vp, i]
         lib.oracle_attn.restype = i
         lib.oracle_attn_quant.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
@@ -87,9 +87,12 @@ def _cpu(t: torch.Tensor) -> torch.Tensor:
     return t.detach().to("cpu").contiguous()
 
 
-def attn(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None,
+def attn(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, window_w=0, rows=None,
          want_lse=False, want_weights=False, nthreads=None):
     """Exact fp64 attention. q: [B,Hq,Nq,D]; k, v: [B,Hkv,Nk,D] (same dtype).
+
+    ``window_w`` > 0: per-row sliding window, row i also needs key
+    j >= pos0 + i - window_w + 1.
 
     ``rows``: optional int64 flat indices (b*Hq + h)*Nq + i. Returns out
     [nrows, D] (or [B,Hq,Nq,D] when rows is None) as float64 numpy, plus lse
@@ -111,8 +114,8 @@ def attn(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None,
     w = np.zeros((nrows, Nk), dtype=np.float64) if want_weights else None
     rc = _load().oracle_attn(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
-        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), float(scale),
-        None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), int(window_w),
+        float(scale), None if rows_arr is None else rows_arr.ctypes.data, nrows,
         out.ctypes.data, None if lse is None else lse.ctypes.data,
         None if w is None else w.ctypes.data, nthreads or default_threads())
     if rc != 0:

@@ -34,7 +34,8 @@
  *
  * Readings taken where the pages are silent (listed again in the design
  * notes): query row i sits at absolute position pos0 + i and key j at j; a
- * key is visible iff j >= window_lo and (not causal or j <= pos0 + i); the KV
+ * key is visible iff j >= window_lo and (not causal or j <= pos0 + i) and,
+ * with a per-row window of width W, j >= pos0 + i - W + 1; the KV
  * head of query head h is h / (Hq / Hkv); a row with no visible key is all
  * zeros ("zeroed inactive regions", section "measured results" of "round 21
  * track b — qsa2"); quantisation blocks are 64 consecutive tokens of one
@@ -99,6 +100,7 @@ typedef struct {
   int dtype;
   int B, Hq, Hkv, Nq, Nk, D;
   int causal, window_lo, pos0;
+  int window_w;          /* > 0: per-row window, key j >= pos0 + i - window_w + 1 */
   double scale;
   const int64_t* rows;   /* NULL: all rows in order */
   int64_t nrows;
@@ -120,6 +122,7 @@ float oracle_e4m3_decode(uint8_t code);
 /* Key j is visible to query row i. */
 static int visible(const attn_job* J, int i, int j) {
   if (j < J->window_lo) return 0;
+  if (J->window_w > 0 && (int64_t)j < (int64_t)J->pos0 + i - J->window_w + 1) return 0;
   if (J->causal && j > J->pos0 + i) return 0;
   return j < J->Nk;
 }
@@ -235,6 +238,10 @@ static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
  *   row-major with D innermost (the "1 x 40 heads x 32 760 tokens x 128"
  *   order of the table in section 1 of "Attention kernels on a home RTX
  *   5080").
+ *   window_w: 0, or a per-row sliding window: row i (position pos0 + i) also
+ *   needs key j >= pos0 + i - window_w + 1 (the per-row reading of the
+ *   "sliding-window lower bound" in the summary of "perf(metal): widen
+ *   four-row flash KV tiles").
  *   rows: flat row indices r = (b*Hq + h)*Nq + i to evaluate, or NULL for all
  *   B*Hq*Nq rows in order; out receives nrows x D doubles.
  *   lse (nullable): m + ln(l) per row, -inf for a row with no visible key.
@@ -243,7 +250,7 @@ static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
  */
 int oracle_attn(const void* q, const void* k, const void* v, int dtype,
                 int B, int Hq, int Hkv, int Nq, int Nk, int D,
-                int causal, int window_lo, int pos0, double scale,
+                int causal, int window_lo, int pos0, int window_w, double scale,
                 const int64_t* rows, int64_t nrows,
                 double* out, double* lse, double* weights, int nthreads) {
   if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
@@ -253,6 +260,7 @@ int oracle_attn(const void* q, const void* k, const void* v, int dtype,
   J.q = q; J.k = k; J.v = v; J.dtype = dtype;
   J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
   J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale;
+  J.window_w = window_w > 0 ? window_w : 0;
   J.rows = rows;
   J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
   J.out = out; J.lse = lse; J.weights = weights;

@@ -269,3 +269,58 @@ def test_input_widening_is_exact_for_every_f16_and_bf16_code():
         k = torch.zeros(1, 1, 1, D, dtype=dt)
         o = oracle.attn(q, k, v, scale=1.0)
         np.testing.assert_array_equal(o.reshape(-1), vals.double().numpy())
+
+
+# ---- per-row sliding window ---------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sliding_window_rows_equal_unmasked_attention_on_their_keys(causal):
+    # row i sees keys [max(0, pos0 + i - W + 1), pos0 + i] (causal) or
+    # [max(0, pos0 + i - W + 1), Nk) (not causal): the same as plain attention of
+    # that one row over exactly those keys
+    B, Hq, Hkv, Nq, Nk, D, W, pos0 = 1, 4, 2, 20, 90, 32, 13, 60
+    q = normal((B, Hq, Nq, D), 1, torch.float32)
+    k = normal((B, Hkv, Nk, D), 2, torch.float32)
+    v = normal((B, Hkv, Nk, D), 3, torch.float32)
+    got = oracle.attn(q, k, v, scale=0.2, causal=causal, pos0=pos0, window_w=W)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        for i in range(Nq):
+            lo = max(0, pos0 + i - W + 1)
+            hi = min(Nk, pos0 + i + 1) if causal else Nk
+            if hi <= lo:
+                assert np.all(got[0, h, i] == 0)
+                continue
+            want = oracle.attn(q[:, h:h + 1, i:i + 1], k[:, g:g + 1, lo:hi].contiguous(),
+                               v[:, g:g + 1, lo:hi].contiguous(), scale=0.2)
+            np.testing.assert_allclose(got[0, h, i], want[0, 0, 0], rtol=1e-13, atol=1e-14)
+
+
+def test_sliding_window_wider_than_the_history_is_no_window():
+    B, Hq, Hkv, Nq, Nk, D, pos0 = 1, 2, 1, 16, 40, 16, 24
+    q, k, v = (normal(s, sd, torch.float16) for s, sd in
+               (((B, Hq, Nq, D), 4), ((B, Hkv, Nk, D), 5), ((B, Hkv, Nk, D), 6)))
+    a = oracle.attn(q, k, v, scale=0.25, causal=True, pos0=pos0)
+    b = oracle.attn(q, k, v, scale=0.25, causal=True, pos0=pos0, window_w=pos0 + Nq)
+    assert np.array_equal(a, b)
+    c = oracle.attn(q, k, v, scale=0.25, causal=True, pos0=pos0, window_w=pos0 + Nq - 1)
+    assert not np.array_equal(a[0, :, Nq - 1], c[0, :, Nq - 1])   # the last row loses key 0
+
+
+def test_sliding_window_of_one_is_the_diagonal_value():
+    # causal, W = 1: row i sees only key pos0 + i, with weight 1
+    B, Hq, Hkv, Nq, Nk, D, pos0 = 1, 3, 3, 10, 30, 8, 17
+    q, k, v = (normal(s, sd, torch.bfloat16) for s, sd in
+               (((B, Hq, Nq, D), 7), ((B, Hkv, Nk, D), 8), ((B, Hkv, Nk, D), 9)))
+    got = oracle.attn(q, k, v, scale=1.0, causal=True, pos0=pos0, window_w=1)
+    want = v[0, :, pos0:pos0 + Nq].double().numpy()
+    assert np.array_equal(got[0], want)
+
+
+def test_sliding_window_single_row_equals_shared_lower_bound():
+    B, Hq, Hkv, Nk, D, W, pos0 = 2, 2, 2, 70, 16, 25, 66
+    q, k, v = (normal(s, sd, torch.float32) for s, sd in
+               (((B, Hq, 1, D), 10), ((B, Hkv, Nk, D), 11), ((B, Hkv, Nk, D), 12)))
+    a = oracle.attn(q, k, v, scale=0.3, causal=True, pos0=pos0, window_w=W)
+    b = oracle.attn(q, k, v, scale=0.3, causal=True, pos0=pos0, window_lo=pos0 - W + 1)
+    assert np.array_equal(a, b)
