@@ -103,6 +103,31 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                 int mode, int dtype);
 
 /*
+ * attn_fwd_sliding — attn_fwd with a per-row sliding window instead of the
+ * shared lower bound: query row i (absolute position pos0 + i) sees key j
+ * only if j >= pos0 + i - window + 1, and, when causal, j <= pos0 + i; so a
+ * causal row sees at most `window` keys, the newest ones. This is the other
+ * reading of the "sliding-window lower bound" in the summary of "perf(metal):
+ * widen four-row flash KV tiles" (there a single bound; here one per row, as
+ * local attention uses it).
+ *
+ *   window     width W >= 1 (ATTN_E_INVALID otherwise).
+ *   workspace  at least attn_fwd_sliding_workspace_bytes(...) bytes.
+ *   Every other argument, the modes, layouts and the error behaviour are
+ *   those of attn_fwd (window_lo is 0 here). Rows with no visible key are
+ *   written as zeros.
+ */
+int attn_fwd_sliding(const void* q, const void* k, const void* v, void* o,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                     int causal, int window, int pos0, float scale, int mode,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace attn_fwd_sliding needs (host-only; 0 for rejected arguments). */
+size_t attn_fwd_sliding_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                        int causal, int window, int pos0, int mode,
+                                        int dtype);
+
+/*
  * attn_quantize_qk — per-block symmetric INT8 codes of Q and K (the "INT8 QK"
  * half of the quantised mode).
  *

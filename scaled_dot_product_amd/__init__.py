@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_workspace_bytes", "quantize_qk", "quantize_v", "decode_kvq",
+__all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_bytes",
+           "quantize_qk", "quantize_v", "decode_kvq",
            "decode_kvq_workspace_bytes", "load_library",
            "MODE_EXACT", "MODE_QUANT", "AttnError", "LIB_PATH"]
 
@@ -45,6 +46,10 @@ def load_library():
     lib.attn_fwd.restype = i
     lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
     lib.attn_fwd_workspace_bytes.restype = sz
+    lib.attn_fwd_sliding.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_fwd_sliding.restype = i
+    lib.attn_fwd_sliding_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
+    lib.attn_fwd_sliding_workspace_bytes.restype = sz
     lib.attn_quantize_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_quantize_qk.restype = i
     lib.attn_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
@@ -85,14 +90,7 @@ def fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos
         _DTYPE[dtype]))
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, window_lo=0,
-        pos0=0, scale=None, mode=MODE_EXACT, out=None, workspace=None) -> torch.Tensor:
-    """O = softmax(scale * Q K^T + mask) V on the current stream.
-
-    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; one dtype (fp32, f16, bf16).
-    Returns O [B, Hq, Nq, D] in q's dtype (written into ``out`` if given).
-    """
-    lib = load_library()
+def _check_qkv(q, k, v):
     _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
         raise AttnError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nk,D]")
@@ -102,25 +100,67 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, wind
     _, Hkv, Nk, Dk = k.shape
     if Dk != D or k.shape[0] != B:
         raise AttnError("q and k disagree on B or D")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    return B, Hq, Hkv, Nq, Nk, D
+
+
+def _out_and_workspace(q, out, workspace, need):
     if out is None:
         out = torch.empty_like(q)
     else:
         _dev(out, "out")
         if out.shape != q.shape or out.dtype != q.dtype:
             raise AttnError("out must match q's shape and dtype")
-    need = fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal=causal, window_lo=window_lo,
-                               pos0=pos0, mode=mode, dtype=q.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return out, ws_ptr, ws_len
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, window_lo=0,
+        pos0=0, scale=None, mode=MODE_EXACT, out=None, workspace=None) -> torch.Tensor:
+    """O = softmax(scale * Q K^T + mask) V on the current stream.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; one dtype (fp32, f16, bf16).
+    Returns O [B, Hq, Nq, D] in q's dtype (written into ``out`` if given).
+    """
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal=causal, window_lo=window_lo,
+                               pos0=pos0, mode=mode, dtype=q.dtype)
+    out, ws_ptr, ws_len = _out_and_workspace(q, out, workspace, need)
     st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo), int(pos0),
                       float(scale), int(mode), _DTYPE[q.dtype], ws_ptr, ws_len,
                       _stream_handle(q))
     _check(st, "attn_fwd")
+    return out
+
+
+def fwd_sliding_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, window, causal=True, pos0=0,
+                                mode=MODE_EXACT, dtype=torch.bfloat16) -> int:
+    return int(load_library().attn_fwd_sliding_workspace_bytes(
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window), int(pos0), int(mode), _DTYPE[dtype]))
+
+
+def fwd_sliding(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window, causal=True,
+                pos0=0, scale=None, mode=MODE_EXACT, out=None, workspace=None) -> torch.Tensor:
+    """Attention with a per-row sliding window: row i sees keys
+    j >= pos0 + i - window + 1 (and j <= pos0 + i when causal)."""
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fwd_sliding_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, window=window, causal=causal,
+                                       pos0=pos0, mode=mode, dtype=q.dtype)
+    out, ws_ptr, ws_len = _out_and_workspace(q, out, workspace, need)
+    st = lib.attn_fwd_sliding(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window), int(pos0),
+                              float(scale), int(mode), _DTYPE[q.dtype], ws_ptr, ws_len,
+                              _stream_handle(q))
+    _check(st, "attn_fwd_sliding")
     return out
 
 

@@ -13,6 +13,8 @@ namespace attn {
 KeyRange key_range(const FwdArgs& a) {
   KeyRange r;
   r.lo = a.window_lo;
+  // the lowest per-row bound is row 0's
+  if (a.window_w > 0 && (int64_t)a.pos0 - a.window_w + 1 > r.lo) r.lo = a.pos0 - a.window_w + 1;
   r.hi = a.causal ? (int)(a.pos0 + (int64_t)a.Nq < a.Nk ? a.pos0 + a.Nq : a.Nk) : a.Nk;
   if (r.hi < r.lo) r.hi = r.lo;
   return r;
@@ -66,7 +68,7 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, int B, i
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
-  a.causal = causal ? 1 : 0; a.window_lo = window_lo; a.pos0 = pos0;
+  a.causal = causal ? 1 : 0; a.window_lo = window_lo; a.pos0 = pos0; a.window_w = 0;
   a.scale = scale;
   // Kept a normal float so that masked scores (-inf) times c stay -inf.
   a.c = fmaxf(scale * kLog2eHost, 1.17549435e-38f);
@@ -113,30 +115,11 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
   return L;
 }
 
-}  // namespace
-}  // namespace attn
-
-using namespace attn;
-
-extern "C" {
-
-size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
-                                int window_lo, int pos0, int mode, int dtype) {
-  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype) != ATTN_OK)
-    return 0;
-  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
-                        window_lo, pos0, 1.0f);
-  return plan_layout(a, mode, dtype).total;
-}
-
-int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
-             int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
-             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
-  if (st != ATTN_OK) return st;
-  if (!q || !k || !v || !o) return ATTN_E_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
-  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+// One validated forward call: workspace check and kernel dispatch.
+int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  const int B = a.B, Hq = a.Hq, Hkv = a.Hkv, Nq = a.Nq, Nk = a.Nk, D = a.D;
+  const void *q = a.q, *k = a.k, *v = a.v;
   const Layout L = plan_layout(a, mode, dtype);
   if (L.total > 0) {
     if (workspace_bytes < L.total) return ATTN_E_WORKSPACE;
@@ -180,6 +163,57 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   else
     e = launch_prefill(a, elem, out_f32, s);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                                int window_lo, int pos0, int mode, int dtype) {
+  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype) != ATTN_OK)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  return plan_layout(a, mode, dtype).total;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+             int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+  return fwd_dispatch(a, mode, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_sliding(const void* q, const void* k, const void* v, void* o, int B, int Hq,
+                     int Hkv, int Nq, int Nk, int D, int causal, int window, int pos0,
+                     float scale, int mode, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, 0, pos0, scale, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (window < 1) return ATTN_E_INVALID;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, 0, pos0, scale);
+  a.window_w = window;
+  return fwd_dispatch(a, mode, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t attn_fwd_sliding_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                        int causal, int window, int pos0, int mode, int dtype) {
+  if (window < 1 || check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, 0, pos0, 1.0f, mode, dtype) != ATTN_OK)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal, 0,
+                        pos0, 1.0f);
+  a.window_w = window;
+  return plan_layout(a, mode, dtype).total;
 }
 
 int attn_quantize_qk(const void* q, const void* k, int8_t* q_codes, float* q_scales,

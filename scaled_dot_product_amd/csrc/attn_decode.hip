@@ -270,6 +270,14 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   const bool cvalid = col < p.rows;
   const int ccol = cvalid ? col : 0;
   const int hh = ccol / a.Nq, qi = ccol - hh * a.Nq;
+  // Column (hh, qi) sees keys [row_lo, row_hi] (none for columns past the
+  // packed rows); tiles inside the bounds common to all rows,
+  // [wave_lo, wave_hi], are not masked.
+  const int wrow = a.window_w > 0 ? a.pos0 - a.window_w + 1 : -(1 << 30);   // row i: key >= i + wrow
+  const int row_lo = cvalid ? max(a.window_lo, qi + wrow) : a.Nk;
+  const int row_hi = a.causal ? min(a.pos0 + qi, a.Nk - 1) : a.Nk - 1;
+  const int wave_lo = max(a.window_lo, a.Nq - 1 + wrow);
+  const int wave_hi = a.causal ? min(a.pos0, a.Nk - 1) : a.Nk - 1;
   const T* Qrow = (const T*)a.q + (((int64_t)b * a.Hq + g * G + hh) * a.Nq + qi) * D;
   V8 qv[KS];
 #pragma unroll
@@ -354,14 +362,13 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
       for (int j = 0; j < 16; ++j) sc[mb][j] = s[mb][0][j] + s[mb][1][j];
     // Only tiles that straddle a bound are masked (columns past the packed
     // rows compute finite values that are never published).
-    if (k0 < a.window_lo || k0 + 64 > a.Nk || (a.causal && k0 + 63 > a.pos0)) {
+    if (k0 < wave_lo || k0 + 63 > wave_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-          const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
-                           (!a.causal || key <= a.pos0 + qi);
+          const bool vis = key >= row_lo && key <= row_hi;
           if (!vis) sc[mb][j] = -INFINITY;
         }
     }
@@ -566,6 +573,14 @@ decode_kvq_kernel(FwdArgs a, DecodeArgs p, const int8_t* __restrict__ kc,
   const bool cvalid = col < p.rows;
   const int ccol = cvalid ? col : 0;
   const int hh = ccol / a.Nq, qi = ccol - hh * a.Nq;
+  // Column (hh, qi) sees keys [row_lo, row_hi] (none for columns past the
+  // packed rows); tiles inside the bounds common to all rows,
+  // [wave_lo, wave_hi], are not masked.
+  const int wrow = a.window_w > 0 ? a.pos0 - a.window_w + 1 : -(1 << 30);   // row i: key >= i + wrow
+  const int row_lo = cvalid ? max(a.window_lo, qi + wrow) : a.Nk;
+  const int row_hi = a.causal ? min(a.pos0 + qi, a.Nk - 1) : a.Nk - 1;
+  const int wave_lo = max(a.window_lo, a.Nq - 1 + wrow);
+  const int wave_hi = a.causal ? min(a.pos0, a.Nk - 1) : a.Nk - 1;
   float x[KS][16];
   float amax = 0.0f;
 #pragma unroll
@@ -660,14 +675,13 @@ decode_kvq_kernel(FwdArgs a, DecodeArgs p, const int8_t* __restrict__ kc,
       for (int j = 0; j < 16; ++j) sf[mb][j] = __builtin_bit_cast(f32x16, s[mb])[j];
     // Only tiles that straddle a bound are masked (columns past the packed
     // rows compute finite values that are never published).
-    if (k0 < a.window_lo || k0 + 64 > a.Nk || (a.causal && k0 + 63 > a.pos0)) {
+    if (k0 < wave_lo || k0 + 63 > wave_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + 32 * half + 16 * mb + 4 * (j >> 2) + (j & 3);
-          const bool vis = cvalid && key >= a.window_lo && key < a.Nk &&
-                           (!a.causal || key <= a.pos0 + qi);
+          const bool vis = key >= row_lo && key <= row_hi;
           if (!vis) sf[mb][j] = -INFINITY;
         }
     }

@@ -18,6 +18,7 @@ struct FwdArgs {
   void* o;
   int B, Hq, Hkv, Nq, Nk, D;
   int causal, window_lo, pos0;
+  int window_w;  // > 0: row i also needs key >= pos0 + i - window_w + 1
   float scale;
   float c;  // scale * log2(e): scores are exponentiated with exp2
 };

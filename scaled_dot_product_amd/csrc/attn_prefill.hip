@@ -89,7 +89,8 @@ prefill_kernel(FwdArgs a, int ntq) {
 
   // Visible keys of this workgroup's rows, as tiles [t_lo, t_lo + nt).
   const int qlast = min(q0 + BM, a.Nq) - 1;
-  const int kv_lo = a.window_lo;
+  // (a per-row window: row q0 has the lowest bound)
+  const int kv_lo = a.window_w > 0 ? max(a.window_lo, a.pos0 + q0 - a.window_w + 1) : a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
   const int t_lo = kv_lo / 64;
   const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
@@ -173,18 +174,23 @@ prefill_kernel(FwdArgs a, int ntq) {
     }
   };
 
-  // Boundary tiles only: window edge, ragged end, causal diagonal.
+  // Row qrow sees keys [row_lo, row_hi]: the shared lower bound, a per-row
+  // window's lower edge, the causal diagonal and the last key. Only tiles
+  // reaching outside the bounds common to the wave's 32 rows are masked.
+  const int wrow = a.window_w > 0 ? a.pos0 - a.window_w + 1 : -(1 << 30);   // row r: key >= r + wrow
+  const int row_lo = max(kv_lo, qrow + wrow);
+  const int row_hi = a.causal ? min(a.pos0 + qrow, a.Nk - 1) : a.Nk - 1;
+  const int wave_lo = max(kv_lo, qw0 + 31 + wrow);                            // largest row_lo
+  const int wave_hi = a.causal ? min(a.pos0 + qw0, a.Nk - 1) : a.Nk - 1;     // smallest row_hi
   auto apply_mask = [&](f32x16 (&s)[2], int t) {
     const int k0 = 64 * t;
-    const bool need = (k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0);
-    if (need) {
+    if (k0 < wave_lo || k0 + 63 > wave_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + 32 * mb + 16 * (j >> 3) + 8 * half + (j & 7);
-          const bool vis = key >= kv_lo && key < a.Nk && (!a.causal || key <= a.pos0 + qrow);
-          if (!vis) s[mb][j] = -INFINITY;
+          if (key < row_lo || key > row_hi) s[mb][j] = -INFINITY;
         }
     }
   };

@@ -219,7 +219,8 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   TO* Op = (TO*)a.o + (int64_t)bh * a.Nq * D;
 
   const int qlast = min(q0 + BM, a.Nq) - 1;
-  const int kv_lo = a.window_lo;
+  // (a per-row window: row q0 has the lowest bound)
+  const int kv_lo = a.window_w > 0 ? max(a.window_lo, a.pos0 + q0 - a.window_w + 1) : a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
   const int t_lo = kv_lo / 64;
   const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
@@ -235,6 +236,14 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 
   const int qrow = q0 + wave * 32 + col;
   const int qw0 = q0 + wave * 32;
+  // Row qrow sees keys [row_lo, row_hi] (shared lower bound, per-row window,
+  // causal diagonal, last key); tiles inside the bounds common to the wave's
+  // rows, [wave_lo, wave_hi], are not masked.
+  const int wrow = a.window_w > 0 ? a.pos0 - a.window_w + 1 : -(1 << 30);   // row r: key >= r + wrow
+  const int row_lo = max(kv_lo, qrow + wrow);
+  const int row_hi = a.causal ? min(a.pos0 + qrow, a.Nk - 1) : a.Nk - 1;
+  const int wave_lo = max(kv_lo, qw0 + 31 + wrow);
+  const int wave_hi = a.causal ? min(a.pos0 + qw0, a.Nk - 1) : a.Nk - 1;
   // Q codes as B operands: lane half h of k-step k holds channels 32 k + 16 h + (0..15).
   i32x4 qv[KS];
 #pragma unroll
@@ -337,14 +346,13 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     // (the whole vector is reinterpreted: a bit cast of one element of the
     // accumulator vector was miscompiled into copies of element 0)
     const int k0 = 64 * t;
-    if ((k0 < kv_lo) || (k0 + 64 > a.Nk) || (a.causal && k0 + 63 > a.pos0 + qw0)) {
+    if (k0 < wave_lo || k0 + 63 > wave_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + 32 * half + 16 * mb + 4 * (j >> 2) + (j & 3);
-          const bool vis = key >= kv_lo && key < a.Nk && (!a.causal || key <= a.pos0 + qrow);
-          if (!vis) sf[mb][j] = -INFINITY;
+          if (key < row_lo || key > row_hi) sf[mb][j] = -INFINITY;
         }
     }
     float mx = sf[0][0];

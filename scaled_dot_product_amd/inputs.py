@@ -36,6 +36,7 @@ class Workload:
     pos0: int = 0
     mode: int = 0          # 0 exact, 1 INT8-QK / FP8-PV, 2 decode over an INT8-K / E4M3-V cache
     scale: float = field(default=float("nan"))
+    window_w: int = 0      # > 0: per-row sliding window, row i sees keys >= pos0 + i - window_w + 1
 
     def __post_init__(self):
         if math.isnan(self.scale):
@@ -58,12 +59,14 @@ class Workload:
         for i in range(self.Nq):
             hi = self.Nk - 1 if not self.causal else min(self.Nk - 1, self.pos0 + i)
             lo = self.window_lo
+            if self.window_w > 0:
+                lo = max(lo, self.pos0 + i - self.window_w + 1)
             total += max(0, hi - lo + 1)
         return total
 
     def flops(self) -> float:
         """4 * D flops per visible (row, key) pair per query head."""
-        if not self.causal and self.window_lo == 0:
+        if not self.causal and self.window_lo == 0 and self.window_w == 0:
             pairs = self.Nq * self.Nk
         else:
             pairs = self.visible_pairs()

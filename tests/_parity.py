@@ -32,8 +32,13 @@ def metrics(o, r):
 def gpu_fwd(w, q, k, v, **kw):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    out = sdpa.fwd(qd, kd, vd, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
-                   scale=w.scale, mode=w.mode, **kw)
+    if w.window_w > 0:
+        assert w.window_lo == 0
+        out = sdpa.fwd_sliding(qd, kd, vd, window=w.window_w, causal=w.causal, pos0=w.pos0,
+                               scale=w.scale, mode=w.mode, **kw)
+    else:
+        out = sdpa.fwd(qd, kd, vd, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                       scale=w.scale, mode=w.mode, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -41,17 +46,18 @@ def gpu_fwd(w, q, k, v, **kw):
 def check_workload(w, rows=None, tol=None, inputs=None):
     """Run w on the GPU and compare (all rows, or a sample) with the oracle."""
     announce(f"{w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} "
-             f"{w.dtype} causal={w.causal} window_lo={w.window_lo} pos0={w.pos0} mode={w.mode}")
+             f"{w.dtype} causal={w.causal} window_lo={w.window_lo} pos0={w.pos0} mode={w.mode} "
+             f"window_w={w.window_w}")
     q, k, v = inputs if inputs is not None else make_qkv(w)
     out = gpu_fwd(w, q, k, v).float().cpu()
     assert torch.isfinite(out).all()
     if rows is None:
         ref = oracle.attn(q, k, v, scale=w.scale, causal=w.causal, window_lo=w.window_lo,
-                          pos0=w.pos0)
+                          pos0=w.pos0, window_w=w.window_w)
         got = out.double().numpy()
     else:
         ref = oracle.attn(q, k, v, scale=w.scale, causal=w.causal, window_lo=w.window_lo,
-                          pos0=w.pos0, rows=rows)
+                          pos0=w.pos0, window_w=w.window_w, rows=rows)
         got = out.reshape(-1, w.D)[torch.from_numpy(rows)].double().numpy()
     rel, mabs = metrics(got, ref)
     print(f"    rel={rel:.3e} max_abs={mabs:.3e}", flush=True)
@@ -66,6 +72,12 @@ def check_workload(w, rows=None, tol=None, inputs=None):
 
 def masked_rows(w):
     """Query rows (per head) that see no key."""
-    if not w.causal:
-        return [] if w.window_lo < w.Nk else list(range(w.Nq))
-    return [i for i in range(w.Nq) if min(w.Nk - 1, w.pos0 + i) < w.window_lo]
+    out = []
+    for i in range(w.Nq):
+        hi = min(w.Nk - 1, w.pos0 + i) if w.causal else w.Nk - 1
+        lo = w.window_lo
+        if w.window_w > 0:
+            lo = max(lo, w.pos0 + i - w.window_w + 1)
+        if hi < lo:
+            out.append(i)
+    return out

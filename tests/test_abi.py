@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
+              "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes",
               "attn_status_string"):
         assert n in names
 
@@ -166,3 +167,36 @@ def test_decode_kvq_workspace_bytes(lib):
     assert ws(1, 64, 1, 1, 4096, 128, 0, 0, 0, 2) == 0        # 64 rows per KV head
     assert ws(1, 32, 1, 1, 4096, 64, 0, 0, 0, 2) > 0          # 32 rows fit
     assert _kvq(lib, ws_bytes=need - 1) == E_WORKSPACE
+
+
+def _sliding(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, D=64,
+             causal=1, window=4, pos0=0, scale=0.125, mode=0, dtype=2,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_sliding(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                                a["Nq"], a["Nk"], a["D"], a["causal"], a["window"], a["pos0"],
+                                a["scale"], a["mode"], a["dtype"], a["ws"], a["ws_bytes"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(window=0), E_INVALID),
+    (dict(window=-3), E_INVALID),
+    (dict(q=None), E_INVALID),
+    (dict(v=FAKE + 4), E_INVALID),
+    (dict(pos0=-1), E_INVALID),
+    (dict(scale=0.0), E_INVALID),
+    (dict(D=80), E_UNSUPPORTED),
+    (dict(mode=1, dtype=0), E_UNSUPPORTED),
+    (dict(dtype=0), E_WORKSPACE),
+])
+def test_sliding_rejects_before_enqueue(lib, kw, want):
+    assert _sliding(lib, **kw) == want
+
+
+def test_sliding_workspace_bytes(lib):
+    ws = lib.attn_fwd_sliding_workspace_bytes
+    assert ws(1, 40, 40, 32760, 32760, 128, 1, 4096, 0, 0, 2) == 0      # bf16 prefill: none
+    assert ws(1, 16, 8, 4, 4096, 128, 1, 1000, 4092, 0, 1) > 0          # decode partials
+    assert ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0, 1) == 0            # window 0 rejected
