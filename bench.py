@@ -6,7 +6,9 @@ in section 1 of "Attention kernels on a home RTX 5080" times its kernels. The
 same run also measures the other shapes of the hot path: the few-row GQA
 decode (cold K/V, rotated over 48 caches so the 256 MB Infinity Cache cannot
 hold them), the quantised INT8-QK / FP8-PV mode on the video shape and the
-SDXL 1024px shape. It prints ONE JSON line.
+SDXL 1024px shape, the causal video shape with a per-row sliding window of
+4096 keys, and the decode over a quantised (INT8 K / E4M3 V) KV cache. It
+prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -74,14 +76,23 @@ def bench_prefill(w, steps, warmup):
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in inputs(w))
     out = torch.empty_like(q)
-    ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
-                                    window_lo=w.window_lo, pos0=w.pos0, mode=w.mode,
-                                    dtype=w.dtype)
+    if w.window_w > 0:
+        ws_n = sdpa.fwd_sliding_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D,
+                                                window=w.window_w, causal=w.causal, pos0=w.pos0,
+                                                mode=w.mode, dtype=w.dtype)
+    else:
+        ws_n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                        window_lo=w.window_lo, pos0=w.pos0, mode=w.mode,
+                                        dtype=w.dtype)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
-                 scale=w.scale, mode=w.mode, out=out, workspace=ws)
+        if w.window_w > 0:
+            sdpa.fwd_sliding(q, k, v, window=w.window_w, causal=w.causal, pos0=w.pos0,
+                             scale=w.scale, mode=w.mode, out=out, workspace=ws)
+        else:
+            sdpa.fwd(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                     scale=w.scale, mode=w.mode, out=out, workspace=ws)
 
     ms = time_events(step, steps, warmup)
     del q, k, v, out, ws
@@ -236,6 +247,15 @@ def run_extra(part):
                            "tflops": round(wc.flops() / (ms_c * 1e-3) / 1e12, 2),
                            "frac_of_bf16_peak": round(wc.flops() / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"causal: {ms_c:.3f} ms/call")
+    elif part == "sliding":
+        wsl = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_sliding4096_bf16_32760",
+                                                        causal=True, window_w=4096)
+        ms_w = bench_prefill(wsl, 10, 2)
+        extra["sliding"] = {"workload": wsl.name, "window": wsl.window_w,
+                            "ms_per_call": round(ms_w, 4),
+                            "tflops": round(wsl.flops() / (ms_w * 1e-3) / 1e12, 2),
+                            "frac_of_bf16_peak": round(wsl.flops() / (ms_w * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"sliding: {ms_w:.3f} ms/call")
     elif part == "sdxl":
         ws_ = WORKLOADS["sdxl_1024px_bf16"]
         ms_s = bench_prefill(ws_, 50, 10)
@@ -339,7 +359,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "causal", "sdxl", "copy"],
+    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "causal", "sliding", "sdxl",
+                                       "copy"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -373,7 +394,7 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "causal", "sdxl", "decode", "decode_kvq"):
+        for part in ("quant", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
             extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)
