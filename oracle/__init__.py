@@ -13,6 +13,8 @@ the definitions and the passages they follow):
 * :func:`e4m3_encode`, :func:`e4m3_decode` — the OCP E4M3 format.
 * :func:`attn_quant` — quantised-mode emulation (diagnostic).
 * :func:`attn_kvq` — exact attention over a quantised KV cache (codes + scales).
+* :func:`quant_mx` — OCP MX FP8 blocks (32 E4M3 elements, one E8M0 scale).
+* :func:`attn_mx` — exact attention on MX-dequantised Q, K, V.
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and library special cases. ``attn_quant`` is
@@ -65,6 +67,10 @@ def _load():
         lib.oracle_attn_kvq.argtypes = [vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
                                         d, i, vp, i64, vp, i]
         lib.oracle_attn_kvq.restype = i
+        lib.oracle_quant_mx.argtypes = [vp, i, i64, i, i, i, vp, vp]
+        lib.oracle_quant_mx.restype = i
+        lib.oracle_attn_mx.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d, vp, i64, vp, i]
+        lib.oracle_attn_mx.restype = i
         lib.oracle_quant_int8.argtypes = [vp, i, i64, i, i, vp, vp]
         lib.oracle_quant_int8.restype = i
         lib.oracle_quant_e4m3.argtypes = [vp, i, i64, i, i, vp, vp]
@@ -185,6 +191,44 @@ def attn_kvq(q, k_codes, k_scales, v_codes, v_scales, *, scale, causal=False, wi
         nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_attn_kvq rejected the arguments")
+    return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+def quant_mx(x, axis=0):
+    """MX FP8 codes (uint8 E4M3, x's layout) and E8M0 scale bytes (uint8):
+    axis 0 -> scales [..., N, D/32]; axis 1 -> scales [..., ceil(N/32), D]."""
+    x = _cpu(x)
+    *lead, N, D = x.shape
+    BH = int(np.prod(lead)) if lead else 1
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    sshape = tuple(lead) + ((N, D // 32) if axis == 0 else ((N + 31) // 32, D))
+    scales = np.zeros(sshape, dtype=np.uint8)
+    rc = _load().oracle_quant_mx(x.data_ptr(), DTYPE_CODE[x.dtype], BH, N, D, int(axis),
+                                 codes.ctypes.data, scales.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_quant_mx rejected the arguments")
+    return codes, scales
+
+
+def attn_mx(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None, nthreads=None):
+    """Exact fp64 attention on MX-dequantised Q, K (blocks along D) and V
+    (blocks along the keys). Same conventions as attn()."""
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if rows is None:
+        nrows, rows_arr = B * Hq * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_attn_mx(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), float(scale),
+        None if rows_arr is None else rows_arr.ctypes.data, nrows, out.ctypes.data,
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_mx rejected the arguments")
     return out.reshape(B, Hq, Nq, D) if rows is None else out
 
 

@@ -31,6 +31,10 @@
  *   oracle_attn_kvq     exact attention over a quantised KV cache: K and V
  *                       given as per-block INT8 / E4M3 codes and scales, Q as
  *                       is or through its own per-block INT8 codes.
+ *   oracle_quant_mx     OCP Microscaling (MX) FP8 blocks: 32 E4M3 elements
+ *                       sharing one power-of-two (E8M0) scale, along D or N.
+ *   oracle_attn_mx      exact attention on MX-dequantised Q, K (blocks along
+ *                       D) and V (blocks along the keys).
  *
  * Readings taken where the pages are silent (listed again in the design
  * notes): query row i sits at absolute position pos0 + i and key j at j; a
@@ -393,6 +397,134 @@ int oracle_quant_e4m3(const void* x, int dtype, int64_t BH, int N, int D,
     }
   }
   return 0;
+}
+
+/* ------------------------------------------------------ MX FP8 blocks -- */
+
+/*
+ * OCP Microscaling (MX) FP8 blocks, the block-scaled format of the MX
+ * variant (per-block-scaled FP8/FP4 in the table of section 1 of "Attention
+ * kernels on a home RTX 5080"; MXFP formats in "Transformers Get a Turbo Boost
+ * with Mixed-Precision Magic"). The pages name the format only; the
+ * definition followed is the OCP Microscaling Formats specification (v1.0):
+ * 32 elements share one scale 2^e stored as an E8M0 byte e + 127, and each
+ * element is an FP8 E4M3 code.
+ *   x: [BH][N][D] of element type dtype; codes: the same layout, uint8 E4M3.
+ *   axis 0: a block is 32 consecutive channels of one token (D % 32 == 0);
+ *           scales [BH][N][D / 32].
+ *   axis 1: a block is 32 consecutive tokens of one channel, the last block
+ *           holding N mod 32 tokens; scales [BH][ceil(N / 32)][D].
+ * Per block: amax = max |x| (fp32). amax == 0 gives scale byte 0 and zero
+ * codes. Otherwise e = floor(log2 amax) - 8, 8 being the exponent of the
+ * largest power of two in E4M3 (256); e is clamped to [-127, 127]; code =
+ * E4M3(clamp(x * 2^-e, -448, 448)) rounded to nearest even (the product is
+ * exact in fp32). Elements of the block above 448 * 2^e saturate.
+ */
+static int mx_block_exp(float amax) {
+  int ex;
+  frexpf(amax, &ex);           /* amax = m * 2^ex, m in [0.5, 1) */
+  int e = (ex - 1) - 8;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+int oracle_quant_mx(const void* x, int dtype, int64_t BH, int N, int D, int axis,
+                    uint8_t* codes, uint8_t* scales) {
+  if (BH < 1 || N < 1 || D < 1) return -1;
+  if (axis == 0 && D % 32 != 0) return -1;
+  if (axis != 0 && axis != 1) return -1;
+  int nb = axis == 0 ? D / 32 : (N + 31) / 32;   /* blocks per token (axis 0) or per head (axis 1) */
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    int outer = axis == 0 ? N : nb;              /* token, or token block */
+    int inner = axis == 0 ? nb : D;              /* channel block, or channel */
+    for (int o = 0; o < outer; ++o) {
+      for (int in = 0; in < inner; ++in) {
+        int64_t idx[32];
+        int cnt = 0;
+        for (int j = 0; j < 32; ++j) {
+          int tok = axis == 0 ? o : 32 * o + j;
+          int ch = axis == 0 ? 32 * in + j : in;
+          if (tok >= N) break;
+          idx[cnt++] = (bh * N + tok) * (int64_t)D + ch;
+        }
+        float amax = 0.0f;
+        for (int j = 0; j < cnt; ++j) {
+          float a = fabsf(load_elem_f(x, dtype, idx[j]));
+          if (a > amax) amax = a;
+        }
+        int64_t sidx = (bh * outer + o) * (int64_t)inner + in;
+        if (amax == 0.0f) {
+          scales[sidx] = 0;
+          for (int j = 0; j < cnt; ++j) codes[idx[j]] = 0;
+          continue;
+        }
+        int e = mx_block_exp(amax);
+        scales[sidx] = (uint8_t)(e + 127);
+        for (int j = 0; j < cnt; ++j) {
+          float y = ldexpf(load_elem_f(x, dtype, idx[j]), -e);
+          if (y > 448.0f) y = 448.0f;
+          if (y < -448.0f) y = -448.0f;
+          codes[idx[j]] = oracle_e4m3_encode(y);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* MX dequantisation into doubles: code value * 2^(scale byte - 127). */
+static int dequant_mx(const void* x, int dtype, int64_t BH, int N, int D, int axis, double* out) {
+  int64_t n = BH * (int64_t)N * D;
+  int64_t ns = axis == 0 ? BH * (int64_t)N * (D / 32) : BH * (int64_t)((N + 31) / 32) * D;
+  uint8_t* c = (uint8_t*)malloc((size_t)n);
+  uint8_t* s = (uint8_t*)malloc((size_t)ns);
+  if (!c || !s || oracle_quant_mx(x, dtype, BH, N, D, axis, c, s) != 0) { free(c); free(s); return -1; }
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t bh = e / ((int64_t)N * D);
+    int tok = (int)((e / D) % N), ch = (int)(e % D);
+    int64_t si = axis == 0 ? (bh * N + tok) * (int64_t)(D / 32) + ch / 32
+                           : (bh * ((N + 31) / 32) + tok / 32) * (int64_t)D + ch;
+    out[e] = ldexp((double)oracle_e4m3_decode(c[e]), (int)s[si] - 127);
+  }
+  free(c); free(s);
+  return 0;
+}
+
+/*
+ * Exact attention (arguments and conventions of oracle_attn, no per-row
+ * window) on the MX dequantisation of Q and K (blocks along D) and of V
+ * (blocks along the keys): the reference of the MX variant up to the
+ * rounding of the softmax weights, which it leaves exact.
+ */
+int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                   int causal, int window_lo, int pos0, double scale,
+                   const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D) || D % 32 != 0) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+  double* qh = (double*)malloc(sizeof(double) * (size_t)nq);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* vh = (double*)malloc(sizeof(double) * (size_t)nk);
+  int rc = -1;
+  if (qh && kh && vh &&
+      dequant_mx(q, dtype, (int64_t)B * Hq, Nq, D, 0, qh) == 0 &&
+      dequant_mx(k, dtype, (int64_t)B * Hkv, Nk, D, 0, kh) == 0 &&
+      dequant_mx(v, dtype, (int64_t)B * Hkv, Nk, D, 1, vh) == 0) {
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+    J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale;
+    J.rows = rows;
+    J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+    J.out = out;
+    J.qhat = qh; J.khat = kh; J.vhat = vh;
+    rc = run_attn(&J, nthreads);
+  }
+  free(qh); free(kh); free(vh);
+  return rc;
 }
 
 /* -------------------------------------------- quantised-mode emulation -- */

@@ -301,3 +301,131 @@ def test_kvq_quantised_q_uses_per_head_blocks():
     np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-5)
     c = oracle.attn_kvq(q, kc, ks, vc, vs, scale=0.125, quant_q=False)
     assert np.abs(a - c).max() > 1e-3   # the quantisation is really applied
+
+
+# ---- OCP MX FP8 blocks (the MX variant) ---------------------------------------
+
+def _mx_deq(codes, scales, axis, N):
+    vals = _f8_values(codes)
+    s = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    if axis == 0:
+        return vals * np.repeat(s, 32, axis=-1)
+    return vals * np.repeat(s, 32, axis=-2)[..., :N, :]
+
+
+def test_mx_named_blocks():
+    x = torch.zeros(1, 4, 64)
+    x[0, 0, :32] = 1.0                      # amax 1: e = -8, 1 -> 256 (0x78)
+    x[0, 0, 32:] = 3.0                      # amax 3: e = -7, 3 -> 384 (0x7C)
+    x[0, 1, :32] = 1.0
+    x[0, 1, 0] = 3.875                      # e = -7; 3.875 -> 496 saturates to 448 (0x7E); 1 -> 128 (0x70)
+    x[0, 1, 1] = 2.0 ** -20                 # 2^-12 after scaling: below half the smallest subnormal -> 0
+    x[0, 1, 2] = -0.5                       # -64 -> 0xE8
+    # row 2, first block stays zero: scale byte 0, zero codes
+    x[0, 2, 32:] = 2.0 ** -130              # below any scale: e clamps to -127
+    c, s = oracle.quant_mx(x, axis=0)
+    assert c[0, 0, 0] == 0x78 and s[0, 0, 0] == 119
+    assert c[0, 0, 40] == 0x7C and s[0, 0, 1] == 120
+    assert c[0, 1, 0] == 0x7E and c[0, 1, 5] == 0x70 and s[0, 1, 0] == 120
+    assert c[0, 1, 1] == 0x00 and c[0, 1, 2] == 0xE8
+    assert s[0, 2, 0] == 0 and np.all(c[0, 2, :32] == 0)
+    assert s[0, 2, 1] == 0   # clamped exponent -127
+
+
+def test_mx_power_of_two_scaling_moves_only_the_scale():
+    x = normal((2, 40, 64), 31, torch.float32)
+    c0, s0 = oracle.quant_mx(x, axis=0)
+    for j in (-5, 3, 11):
+        c1, s1 = oracle.quant_mx(x * 2.0 ** j, axis=0)
+        assert np.array_equal(c0, c1)
+        assert np.array_equal(s1.astype(int) - s0.astype(int), np.full(s0.shape, j))
+
+
+def test_mx_axes_agree_under_transpose():
+    x = normal((3, 64, 96), 32, torch.bfloat16)
+    c1, s1 = oracle.quant_mx(x, axis=1)                         # blocks along N
+    c0, s0 = oracle.quant_mx(x.transpose(1, 2).contiguous(), axis=0)   # the same blocks along D
+    assert np.array_equal(c1, c0.transpose(0, 2, 1))
+    assert np.array_equal(s1, s0.transpose(0, 2, 1))
+
+
+def test_mx_partial_last_block_along_n():
+    x = torch.full((1, 70, 32), 0.25, dtype=torch.float16)
+    x[0, 64:, :] = 5.0                       # the last block (tokens 64..69) alone has amax 5
+    x[0, 10, 3] = -1.0
+    c, s = oracle.quant_mx(x, axis=1)
+    assert s.shape == (1, 3, 32)
+    assert s[0, 0, 3] == 127 - 8             # channel 3 of block 0: amax 1, e = -8
+    assert np.all(np.delete(s[0, 0], 3) == 127 - 10)   # amax 0.25: e = -10
+    assert np.all(s[0, 1] == 127 - 10)
+    assert np.all(s[0, 2] == 127 - 6)        # tokens 64..69 only: amax 5, e = -6
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_mx_elements_match_torch_cast_and_error_bound(dtype):
+    x = normal((2, 50, 128), 33, dtype)
+    for axis in (0, 1):
+        c, s = oracle.quant_mx(x, axis=axis)
+        xf = x.double().numpy()
+        if axis == 0:
+            e = np.repeat(s.astype(np.int64) - 127, 32, axis=-1)
+        else:
+            e = np.repeat(s.astype(np.int64) - 127, 32, axis=-2)[..., :50, :]
+        y = np.clip(np.ldexp(xf, -e), -448, 448).astype(np.float32)
+        want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(c, want)
+        deq = _mx_deq(c, s, axis, 50)
+        a = np.abs(xf)
+        normal_range = (np.ldexp(a, -e) >= 2.0 ** -6) & (np.ldexp(a, -e) <= 448)
+        assert np.all(np.abs(deq - xf)[normal_range] <= 2.0 ** -4 * a[normal_range])
+        assert np.all(np.abs(deq - xf)[~normal_range & (np.ldexp(a, -e) < 1)]
+                      <= np.ldexp(2.0 ** -10, e)[~normal_range & (np.ldexp(a, -e) < 1)])
+
+
+def _mx_grid(rng, shape, axis):
+    """Values exactly on the MX grid: E4M3 values times 2^e per 32-block, each
+    block holding one +-256 * 2^e element so that its scale is exactly 2^e."""
+    mags = np.array([oracle.e4m3_decode(c) for c in range(0x7F)])
+    vals = rng.choice(mags[mags <= 240], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+    if axis == 0:
+        *lead, N, D = shape
+        e = rng.integers(-12, -6, size=tuple(lead) + (N, D // 32))
+        vals[..., ::32] = 256.0 * rng.choice([-1.0, 1.0], size=vals[..., ::32].shape)
+        return vals * np.ldexp(1.0, np.repeat(e, 32, axis=-1))
+    *lead, N, D = shape
+    e = rng.integers(-12, -6, size=tuple(lead) + ((N + 31) // 32, D))
+    vals[..., ::32, :] = 256.0 * rng.choice([-1.0, 1.0], size=vals[..., ::32, :].shape)
+    return vals * np.ldexp(1.0, np.repeat(e, 32, axis=-2)[..., :N, :])
+
+
+@pytest.mark.parametrize("causal,window_lo,pos0", [(False, 0, 0), (True, 0, 40), (True, 17, 10)])
+def test_mx_attention_on_grid_inputs_is_exact_attention(causal, window_lo, pos0):
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, Nq, Nk, D = 1, 4, 2, 24, 70, 64
+    q = torch.from_numpy(_mx_grid(rng, (B, Hq, Nq, D), 0).astype(np.float32))
+    k = torch.from_numpy(_mx_grid(rng, (B, Hkv, Nk, D), 0).astype(np.float32))
+    v = torch.from_numpy(_mx_grid(rng, (B, Hkv, Nk, D), 1).astype(np.float32))
+    for t, axis in ((q, 0), (k, 0), (v, 1)):
+        c, s = oracle.quant_mx(t, axis=axis)
+        assert np.array_equal(_mx_deq(c, s, axis, t.shape[2]), t.double().numpy())
+    a = oracle.attn_mx(q, k, v, scale=0.1, causal=causal, window_lo=window_lo, pos0=pos0)
+    b = oracle.attn(q, k, v, scale=0.1, causal=causal, window_lo=window_lo, pos0=pos0)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_mx_attention_quantises_all_three_inputs():
+    # off the grid each of Q, K, V changes the result (a dropped quantisation fails)
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 2, 16, 96, 64
+    q, k, v = (normal(s_, sd, torch.float32) for s_, sd in
+               (((B, Hq, Nq, D), 41), ((B, Hkv, Nk, D), 42), ((B, Hkv, Nk, D), 43)))
+    base = oracle.attn_mx(q, k, v, scale=0.125)
+    exact = oracle.attn(q, k, v, scale=0.125)
+    rel = np.linalg.norm(base - exact) / np.linalg.norm(exact)
+    assert 1e-3 < rel < 6e-2
+    for which in range(3):
+        t = [q, k, v]
+        c, s = oracle.quant_mx(t[which], axis=1 if which == 2 else 0)
+        t[which] = torch.from_numpy(_mx_deq(c, s, 1 if which == 2 else 0, t[which].shape[2]).astype(np.float32))
+        # quantising an input twice changes nothing: the grid is a fixed point
+        again = oracle.attn_mx(*t, scale=0.125)
+        np.testing.assert_allclose(again, base, rtol=1e-6, atol=1e-7)
