@@ -14,7 +14,7 @@ the definitions and the passages they follow):
 * :func:`attn_quant` — quantised-mode emulation (diagnostic).
 * :func:`attn_kvq` — exact attention over a quantised KV cache (codes + scales).
 * :func:`quant_mx` — OCP MX FP8 blocks (32 E4M3 elements, one E8M0 scale).
-* :func:`attn_mx` — exact attention on MX-dequantised Q, K, V.
+* :func:`attn_mx` — exact attention on the MX variant's inputs (INT8 Q, K; MX V).
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and library special cases. ``attn_quant`` is
@@ -211,8 +211,9 @@ def quant_mx(x, axis=0):
 
 
 def attn_mx(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None, nthreads=None):
-    """Exact fp64 attention on MX-dequantised Q, K (blocks along D) and V
-    (blocks along the keys). Same conventions as attn()."""
+    """Exact fp64 attention on the MX variant's inputs: Q and K through their
+    per-64-token INT8 blocks, V through MX blocks of 32 keys. Same conventions
+    as attn()."""
     q, k, v = _cpu(q), _cpu(k), _cpu(v)
     B, Hq, Nq, D = q.shape
     _, Hkv, Nk, _ = k.shape

@@ -33,8 +33,8 @@
  *                       is or through its own per-block INT8 codes.
  *   oracle_quant_mx     OCP Microscaling (MX) FP8 blocks: 32 E4M3 elements
  *                       sharing one power-of-two (E8M0) scale, along D or N.
- *   oracle_attn_mx      exact attention on MX-dequantised Q, K (blocks along
- *                       D) and V (blocks along the keys).
+ *   oracle_attn_mx      exact attention on the MX variant's inputs: INT8
+ *                       Q, K blocks and V in MX blocks along the keys.
  *
  * Readings taken where the pages are silent (listed again in the design
  * notes): query row i sits at absolute position pos0 + i and key j at j; a
@@ -473,6 +473,8 @@ int oracle_quant_mx(const void* x, int dtype, int64_t BH, int N, int D, int axis
   return 0;
 }
 
+static int dequant_int8(const void* x, int dtype, int64_t BH, int N, int D, double* out);
+
 /* MX dequantisation into doubles: code value * 2^(scale byte - 127). */
 static int dequant_mx(const void* x, int dtype, int64_t BH, int N, int D, int axis, double* out) {
   int64_t n = BH * (int64_t)N * D;
@@ -493,8 +495,9 @@ static int dequant_mx(const void* x, int dtype, int64_t BH, int N, int D, int ax
 
 /*
  * Exact attention (arguments and conventions of oracle_attn, no per-row
- * window) on the MX dequantisation of Q and K (blocks along D) and of V
- * (blocks along the keys): the reference of the MX variant up to the
+ * window) on the inputs of the MX variant: Q and K through their per-64-token
+ * INT8 blocks (oracle_quant_int8) and V through MX blocks of 32 keys
+ * (oracle_quant_mx, axis 1). This is the MX variant's reference up to the
  * rounding of the softmax weights, which it leaves exact.
  */
 int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
@@ -509,8 +512,8 @@ int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
   double* vh = (double*)malloc(sizeof(double) * (size_t)nk);
   int rc = -1;
   if (qh && kh && vh &&
-      dequant_mx(q, dtype, (int64_t)B * Hq, Nq, D, 0, qh) == 0 &&
-      dequant_mx(k, dtype, (int64_t)B * Hkv, Nk, D, 0, kh) == 0 &&
+      dequant_int8(q, dtype, (int64_t)B * Hq, Nq, D, qh) == 0 &&
+      dequant_int8(k, dtype, (int64_t)B * Hkv, Nk, D, kh) == 0 &&
       dequant_mx(v, dtype, (int64_t)B * Hkv, Nk, D, 1, vh) == 0) {
     attn_job J;
     memset(&J, 0, sizeof J);

@@ -382,39 +382,43 @@ def test_mx_elements_match_torch_cast_and_error_bound(dtype):
                       <= np.ldexp(2.0 ** -10, e)[~normal_range & (np.ldexp(a, -e) < 1)])
 
 
-def _mx_grid(rng, shape, axis):
-    """Values exactly on the MX grid: E4M3 values times 2^e per 32-block, each
-    block holding one +-256 * 2^e element so that its scale is exactly 2^e."""
+def _mx_grid(rng, shape):
+    """Values exactly on the MX grid along N: E4M3 values times 2^e per block
+    of 32 tokens of a channel, each block holding one +-256 * 2^e element so
+    that its scale is exactly 2^e."""
     mags = np.array([oracle.e4m3_decode(c) for c in range(0x7F)])
     vals = rng.choice(mags[mags <= 240], size=shape) * rng.choice([-1.0, 1.0], size=shape)
-    if axis == 0:
-        *lead, N, D = shape
-        e = rng.integers(-12, -6, size=tuple(lead) + (N, D // 32))
-        vals[..., ::32] = 256.0 * rng.choice([-1.0, 1.0], size=vals[..., ::32].shape)
-        return vals * np.ldexp(1.0, np.repeat(e, 32, axis=-1))
     *lead, N, D = shape
     e = rng.integers(-12, -6, size=tuple(lead) + ((N + 31) // 32, D))
     vals[..., ::32, :] = 256.0 * rng.choice([-1.0, 1.0], size=vals[..., ::32, :].shape)
     return vals * np.ldexp(1.0, np.repeat(e, 32, axis=-2)[..., :N, :])
 
 
+def _int8_grid(rng, shape):
+    """Integer codes times 2^-5 with a 127 in every 64-token block: the INT8
+    rule reproduces them exactly (scale 2^-5, inverse 2^5)."""
+    x = rng.integers(-126, 127, size=shape).astype(np.float64)
+    x[..., ::64, 0] = 127.0
+    return np.ldexp(x, -5)
+
+
 @pytest.mark.parametrize("causal,window_lo,pos0", [(False, 0, 0), (True, 0, 40), (True, 17, 10)])
 def test_mx_attention_on_grid_inputs_is_exact_attention(causal, window_lo, pos0):
     rng = np.random.default_rng(12)
     B, Hq, Hkv, Nq, Nk, D = 1, 4, 2, 24, 70, 64
-    q = torch.from_numpy(_mx_grid(rng, (B, Hq, Nq, D), 0).astype(np.float32))
-    k = torch.from_numpy(_mx_grid(rng, (B, Hkv, Nk, D), 0).astype(np.float32))
-    v = torch.from_numpy(_mx_grid(rng, (B, Hkv, Nk, D), 1).astype(np.float32))
-    for t, axis in ((q, 0), (k, 0), (v, 1)):
-        c, s = oracle.quant_mx(t, axis=axis)
-        assert np.array_equal(_mx_deq(c, s, axis, t.shape[2]), t.double().numpy())
+    q = torch.from_numpy(_int8_grid(rng, (B, Hq, Nq, D)).astype(np.float32))
+    k = torch.from_numpy(_int8_grid(rng, (B, Hkv, Nk, D)).astype(np.float32))
+    v = torch.from_numpy(_mx_grid(rng, (B, Hkv, Nk, D)).astype(np.float32))
+    c, s_ = oracle.quant_mx(v, axis=1)
+    assert np.array_equal(_mx_deq(c, s_, 1, Nk), v.double().numpy())
     a = oracle.attn_mx(q, k, v, scale=0.1, causal=causal, window_lo=window_lo, pos0=pos0)
     b = oracle.attn(q, k, v, scale=0.1, causal=causal, window_lo=window_lo, pos0=pos0)
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
 
 
 def test_mx_attention_quantises_all_three_inputs():
-    # off the grid each of Q, K, V changes the result (a dropped quantisation fails)
+    # off the grid each of Q, K (INT8) and V (MX) changes the result; feeding
+    # the dequantised values back in changes nothing (the grids are fixed points)
     B, Hq, Hkv, Nq, Nk, D = 1, 2, 2, 16, 96, 64
     q, k, v = (normal(s_, sd, torch.float32) for s_, sd in
                (((B, Hq, Nq, D), 41), ((B, Hkv, Nk, D), 42), ((B, Hkv, Nk, D), 43)))
@@ -422,10 +426,15 @@ def test_mx_attention_quantises_all_three_inputs():
     exact = oracle.attn(q, k, v, scale=0.125)
     rel = np.linalg.norm(base - exact) / np.linalg.norm(exact)
     assert 1e-3 < rel < 6e-2
-    for which in range(3):
-        t = [q, k, v]
-        c, s = oracle.quant_mx(t[which], axis=1 if which == 2 else 0)
-        t[which] = torch.from_numpy(_mx_deq(c, s, 1 if which == 2 else 0, t[which].shape[2]).astype(np.float32))
-        # quantising an input twice changes nothing: the grid is a fixed point
-        again = oracle.attn_mx(*t, scale=0.125)
-        np.testing.assert_allclose(again, base, rtol=1e-6, atol=1e-7)
+    t = [q, k, v]
+    for which in (0, 1):
+        c, s_ = oracle.quant_int8(t[which])
+        n = t[which].shape[2]
+        t[which] = torch.from_numpy((c.astype(np.float64) *
+                                     np.repeat(s_.astype(np.float64), 64, axis=-1)[..., :n, None])
+                                    .astype(np.float32))
+    c, s_ = oracle.quant_mx(t[2], axis=1)
+    t[2] = torch.from_numpy(_mx_deq(c, s_, 1, Nk).astype(np.float32))
+    np.testing.assert_allclose(oracle.attn_mx(*t, scale=0.125), base, rtol=1e-5, atol=1e-6)
+    # and the same values as plain inputs give the same attention
+    np.testing.assert_allclose(oracle.attn(*t, scale=0.125), base, rtol=1e-5, atol=1e-6)
