@@ -5,7 +5,8 @@ One step is one attention forward of the video-DiT workload (B=1, 40 heads,
 in section 1 of "Attention kernels on a home RTX 5080" times its kernels. The
 same run also measures the other shapes of the hot path: the few-row GQA
 decode (cold K/V, rotated over 48 caches so the 256 MB Infinity Cache cannot
-hold them), the quantised INT8-QK / FP8-PV mode on the video shape and the
+hold them), the quantised INT8-QK / FP8-PV mode and the MX mode (MX FP8
+blocks on the P V product) on the video shape, the
 SDXL 1024px shape, the causal video shape with a per-row sliding window of
 4096 keys, and the decode over a quantised (INT8 K / E4M3 V) KV cache. It
 prints ONE JSON line.
@@ -240,6 +241,13 @@ def run_extra(part):
                           "kernel_tops_est": round(wq.flops() / ((ms_q - ms_prep) * 1e-3) / 1e12, 2),
                           "frac_of_fp8_peak": round(wq.flops() / (ms_q * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
         log(f"quant: {ms_q:.3f} ms/call incl. {ms_prep:.3f} ms preparation")
+    elif part == "mx":
+        wm = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_mx_32760", mode=2)
+        ms_m = bench_prefill(wm, 10, 2)
+        extra["mx"] = {"workload": wm.name, "ms_per_call": round(ms_m, 4),
+                       "tops": round(wm.flops() / (ms_m * 1e-3) / 1e12, 2),
+                       "frac_of_fp8_peak": round(wm.flops() / (ms_m * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        log(f"mx: {ms_m:.3f} ms/call incl. preparation")
     elif part == "causal":
         wc = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_causal_bf16_32760", causal=True)
         ms_c = bench_prefill(wc, 10, 2)
@@ -359,8 +367,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "causal", "sliding", "sdxl",
-                                       "copy"],
+    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "mx", "causal", "sliding",
+                                       "sdxl", "copy"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -394,7 +402,7 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
+        for part in ("quant", "mx", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
             extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)

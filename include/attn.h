@@ -53,10 +53,19 @@ typedef enum { ATTN_DT_F32 = 0, ATTN_DT_F16 = 1, ATTN_DT_BF16 = 2 } attn_dtype;
 typedef enum {
   ATTN_MODE_EXACT = 0, /* bf16/f16 matrix products, fp32 accumulation and
                           softmax; fp32 inputs are rounded to bf16 first */
-  ATTN_MODE_QUANT = 1  /* INT8 Q K^T and FP8 (E4M3) P V with per-block
+  ATTN_MODE_QUANT = 1, /* INT8 Q K^T and FP8 (E4M3) P V with per-block
                           scales ("SageAttention 2 INT8 QK . FP8 PV" row of
                           the table in section 1 of "Attention kernels on a
                           home RTX 5080"); bf16/f16 inputs only */
+  ATTN_MODE_MX = 2     /* OCP MX FP8 blocks everywhere: Q and K in blocks of
+                          32 channels, V in blocks of 32 keys (attn_quantize_mx),
+                          the softmax weights in blocks of 32 keys of each row;
+                          both products on the scaled FP8 matrix cores with
+                          the E8M0 block scales as operands (the per-block-
+                          scaled low-precision kernels of that table, MXFP as
+                          in "Transformers Get a Turbo Boost with
+                          Mixed-Precision Magic"); bf16/f16 inputs only; head
+                          dim 64 or 128 */
 } attn_mode;
 
 /*
@@ -160,6 +169,24 @@ int attn_quantize_qk(const void* q, const void* k, int8_t* q_codes, float* q_sca
  */
 int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales,
                     int B, int Hkv, int Nk, int D, int dtype, void* stream);
+
+/*
+ * attn_quantize_mx — OCP Microscaling (MX) FP8 blocks of the MX mode: 32
+ * elements share one power-of-two scale 2^e, stored as an E8M0 byte e + 127,
+ * and each element is an OCP FP8 E4M3 code. Per block, in fp32: amax = max
+ * |x|; amax == 0 gives scale byte 0 and zero codes; otherwise e = floor(log2
+ * amax) - 8 clamped to [-127, 127] and code = E4M3(clamp(x * 2^-e, -448,
+ * 448)) rounded to nearest even (elements above 448 * 2^e saturate).
+ *
+ *   x        device [B][H][N][D], bf16/f16 (`dtype`); D = 64 or 128.
+ *   codes    device uint8 [B][H][N][D].
+ *   scales   device uint8: axis 0 (blocks of 32 consecutive channels of one
+ *            token) [B][H][N][D/32]; axis 1 (blocks of 32 consecutive tokens
+ *            of one channel, the last holding N mod 32) [B][H][ceil(N/32)][D].
+ * Codes and scales are bit-exact with the CPU oracle's definition.
+ */
+int attn_quantize_mx(const void* x, uint8_t* codes, uint8_t* scales, int B, int H, int N,
+                     int D, int axis, int dtype, void* stream);
 
 /*
  * attn_decode_kvq — decode over a quantised KV cache: the split-KV decode of

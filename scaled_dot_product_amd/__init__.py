@@ -16,14 +16,15 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_bytes",
-           "quantize_qk", "quantize_v", "decode_kvq",
+           "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
            "decode_kvq_workspace_bytes", "load_library",
-           "MODE_EXACT", "MODE_QUANT", "AttnError", "LIB_PATH"]
+           "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 MODE_EXACT = 0
 MODE_QUANT = 1
+MODE_MX = 2
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _lib = None
@@ -54,6 +55,8 @@ def load_library():
     lib.attn_quantize_qk.restype = i
     lib.attn_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     lib.attn_quantize_v.restype = i
+    lib.attn_quantize_mx.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.attn_quantize_mx.restype = i
     lib.attn_decode_kvq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
                                      vp, sz, vp]
     lib.attn_decode_kvq.restype = i
@@ -192,6 +195,22 @@ def quantize_v(v: torch.Tensor):
                              _DTYPE.get(v.dtype, -1), _stream_handle(v))
     _check(st, "attn_quantize_v")
     return vc, vs
+
+
+def quantize_mx(x: torch.Tensor, axis: int = 0):
+    """OCP MX FP8 codes (uint8 E4M3, x's layout) and E8M0 scale bytes (uint8) of
+    x [B, H, N, D] (bf16/f16): axis 0 -> scales [B, H, N, D/32] (blocks of 32
+    channels), axis 1 -> scales [B, H, ceil(N/32), D] (blocks of 32 tokens)."""
+    lib = load_library()
+    _dev(x, "x")
+    B, H, N, D = x.shape
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    sshape = (B, H, N, D // 32) if axis == 0 else (B, H, (N + 31) // 32, D)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    st = lib.attn_quantize_mx(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, D,
+                              int(axis), _DTYPE.get(x.dtype, -1), _stream_handle(x))
+    _check(st, "attn_quantize_mx")
+    return codes, scales
 
 
 def decode_kvq_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos0=0,

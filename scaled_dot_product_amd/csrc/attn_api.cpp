@@ -41,8 +41,9 @@ int check_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int win
   if (st != ATTN_OK) return st;
   if (window_lo < 0 || pos0 < 0) return ATTN_E_INVALID;
   if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_E_INVALID;
-  if (mode != ATTN_MODE_EXACT && mode != ATTN_MODE_QUANT) return ATTN_E_UNSUPPORTED;
-  if (mode == ATTN_MODE_QUANT && dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (mode != ATTN_MODE_EXACT && mode != ATTN_MODE_QUANT && mode != ATTN_MODE_MX)
+    return ATTN_E_UNSUPPORTED;
+  if (mode != ATTN_MODE_EXACT && dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -90,6 +91,17 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
   size_t off = 0;
   const size_t nq = (size_t)a.B * a.Hq * a.Nq * a.D;
   const size_t nk = (size_t)a.B * a.Hkv * a.Nk * a.D;
+  if (mode == ATTN_MODE_MX) {
+    const size_t tiles = (size_t)(a.Nk + 63) / 64;
+    L.qc = off; off = round_up(off + nq);
+    L.qs = off; off = round_up(off + (size_t)a.B * a.Hq * ((a.Nq + 63) / 64) * 4);
+    L.kc = off; off = round_up(off + nk);
+    L.ks = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 4);
+    L.vc = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 64 * a.D);
+    L.vs = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 2 * a.D);
+    L.total = off;
+    return L;
+  }
   if (mode == ATTN_MODE_QUANT) {
     const size_t tiles = (size_t)(a.Nk + 63) / 64;
     L.qc = off; off = round_up(off + nq);
@@ -129,6 +141,22 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   char* ws = (char*)workspace;
   hipError_t e = hipSuccess;
 
+  if (mode == ATTN_MODE_MX) {
+    const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+    e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
+                          (float*)(ws + L.qs), s);
+    if (e == hipSuccess)
+      e = launch_quant_int8(k, elem, (int64_t)B * Hkv, Nk, D, (int8_t*)(ws + L.kc),
+                            (float*)(ws + L.ks), s);
+    if (e == hipSuccess)
+      e = launch_quant_mx(v, elem, (int64_t)B * Hkv, Nk, D, 1, 1, 0, (uint8_t*)(ws + L.vc),
+                          (uint8_t*)(ws + L.vs), s);
+    if (e == hipSuccess)
+      e = launch_prefill_mx(a, (const int8_t*)(ws + L.qc), (const float*)(ws + L.qs),
+                            (const int8_t*)(ws + L.kc), (const float*)(ws + L.ks),
+                            (const uint8_t*)(ws + L.vc), (const uint8_t*)(ws + L.vs), elem, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  }
   if (mode == ATTN_MODE_QUANT) {
     const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
     e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
@@ -243,6 +271,20 @@ int attn_quantize_v(const void* v, uint8_t* v_codes, float* v_scales, int B, int
   const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
   hipError_t e = launch_quant_e4m3(v, elem, (int64_t)B * Hkv, Nk, D, v_codes, v_scales, 0,
                                    (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_quantize_mx(const void* x, uint8_t* codes, uint8_t* scales, int B, int H, int N, int D,
+                     int axis, int dtype, void* stream) {
+  int st = check_shape(B, H, H, N, 1, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (axis != 0 && axis != 1) return ATTN_E_INVALID;
+  if (!x || !codes || !scales) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(codes)) return ATTN_E_INVALID;
+  const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+  const hipError_t e = launch_quant_mx(x, elem, (int64_t)B * H, N, D, axis, 0, N, codes, scales,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

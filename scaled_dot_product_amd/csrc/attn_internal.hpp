@@ -69,4 +69,17 @@ hipError_t launch_prefill_quant(const FwdArgs& a, const int8_t* qc, const float*
                                 const int8_t* kc, const float* ks, const uint8_t* vct,
                                 const float* vs, int elem_out, hipStream_t s);
 
+// ---- MX variant (OCP MX FP8 blocks, scaled FP8 MFMA) ----------------------
+// axis 0: blocks of 32 channels, scales [BH][srows][D/32] (srows >= N);
+// axis 1: blocks of 32 tokens; layout 0: codes [BH][N][D], scales
+// [BH][ceil(N/32)][D]; layout 1: codes [BH][ceil(N/64)][D][64] (zero past N),
+// scales [BH][2 ceil(N/64)][D].
+hipError_t launch_quant_mx(const void* x, int elem, int64_t BH, int N, int D, int axis, int layout,
+                           int srows, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Q and K as per-64-token INT8 blocks (launch_quant_int8), V as MX
+// transposed tiles + scale bytes (axis 1, layout 1).
+hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs,
+                             const int8_t* kc, const float* ks, const uint8_t* vct,
+                             const uint8_t* vs, int elem_out, hipStream_t s);
+
 }  // namespace attn

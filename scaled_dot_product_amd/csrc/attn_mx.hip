@@ -1,0 +1,492 @@
+// attn_mx.hip — the MX variant: OCP Microscaling FP8 blocks on the scaled
+// FP8 matrix cores of gfx950.
+//
+// The table in section 1 of "Attention kernels on a home RTX 5080" puts
+// per-block-scaled low-precision kernels at the top of its speed list, and
+// "Transformers Get a Turbo Boost with Mixed-Precision Magic" runs attention
+// on MXFP formats. Neither gives the arithmetic, so the format is the OCP
+// Microscaling (MX) one: 32 FP8 E4M3 elements share one power-of-two scale
+// stored as an E8M0 byte. gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 takes one
+// such scale per lane and 32-element block of each operand, so the matrix
+// core applies every block scale of the P V product itself.
+//
+// Q K^T stays in the per-64-token-block INT8 of the quantised mode: the INT8
+// matrix cores run at the FP8 rate, and E4M3 on Q and K alone costs about
+// 3.5 % relative error, which with V's and P's E4M3 rounding would use up
+// the 6 % budget.
+//
+// MX quantisation follows the OCP rule: e = floor(log2 amax) - 8, code =
+// E4M3(clamp(x * 2^-e, +-448)) rounded to nearest even.
+#include "attn_common.hpp"
+#include "attn_internal.hpp"
+
+namespace attn {
+
+namespace {
+
+// Block exponent of the OCP rule from a block maximum (> 0): floor(log2 amax)
+// - 8, clamped to the E8M0 range [-127, 127].
+__device__ __forceinline__ int mx_exp(float amax) {
+  const int ex = __builtin_amdgcn_frexp_expf(amax);   // amax = m 2^ex, m in [0.5, 1)
+  return min(max(ex - 1 - 8, -127), 127);
+}
+
+// Four E4M3 codes of x * 2^-e (clamped to +-448), packed little-endian.
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, int e) {
+  auto y = [&](float x) { return fminf(fmaxf(__builtin_amdgcn_ldexpf(x, -e), -448.0f), 448.0f); };
+  int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y(a), y(b), 0, false);
+  pk = __builtin_amdgcn_cvt_pk_fp8_f32(y(c), y(d), pk, true);
+  return (uint32_t)pk;
+}
+
+// Blocks of 32 channels: one thread per (token, block). Scales go to
+// [BH][srows][D / 32] with srows >= N rows per head (padding rows untouched).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) quant_mx_rows_kernel(const T* __restrict__ x, int64_t BH,
+                                                            int N, int srows,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  constexpr int NB = D / 32;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= BH * N * NB) return;
+  const int64_t row = id / NB;
+  const int blk = (int)(id - row * NB);
+  const int64_t bh = row / N;
+  const int tok = (int)(row - bh * N);
+  const T* src = x + row * D + 32 * blk;
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) unpack8<T>(ld16(src + 8 * c), &v[8 * c]);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint8_t sb = 0;
+  if (amax > 0.0f) {
+    const int e = mx_exp(amax);
+    sb = (uint8_t)(e + 127);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], e);
+  }
+  uint8_t* dst = codes + row * D + 32 * blk;
+  st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+  st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+  scales[(bh * srows + tok) * NB + blk] = sb;
+}
+
+// Blocks of 32 tokens of one channel: one workgroup per (head, 64-token tile).
+// layout 0: codes [BH][N][D], scales [BH][ceil(N/32)][D] (blocks past N not
+//           written);
+// layout 1: codes as transposed tiles [BH][ceil(N/64)][D][64] with zero codes
+//           past N, scales [BH][2 ceil(N/64)][D] (a block past N: scale byte 0).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict__ x, int N,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            int layout) {
+  constexpr int CPR = D / 8;
+  constexpr int TLD = D + 1;
+  __shared__ float tile[64 * TLD];
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[64 * D];
+  const int nt = (N + 63) / 64;
+  const int64_t bh = blockIdx.x / nt;
+  const int t = (int)(blockIdx.x - bh * nt);
+  const int r0 = 64 * t;
+  const T* src = x + (bh * N + r0) * (int64_t)D;
+  for (int ch = threadIdx.x; ch < 64 * CPR; ch += 256) {
+    const int r = ch / CPR, c = ch - r * CPR;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (r0 + r < N) unpack8<T>(ld16(src + (int64_t)r * D + 8 * c), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r * TLD + 8 * c + i] = v[i];
+  }
+  __syncthreads();
+  const int nblk32 = (N + 31) / 32;
+  for (int task = threadIdx.x; task < 2 * D; task += 256) {
+    const int d = task % D, j = task / D;
+    const int tok0 = r0 + 32 * j;
+    const int cnt = min(max(N - tok0, 0), 32);
+    float amax = 0.0f;
+    for (int i = 0; i < cnt; ++i) amax = fmaxf(amax, fabsf(tile[(32 * j + i) * TLD + d]));
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint8_t sb = 0;
+    if (amax > 0.0f) {
+      const int e = mx_exp(amax);
+      sb = (uint8_t)(e + 127);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float* col = &tile[(32 * j + 4 * q) * TLD + d];
+        w[q] = mx_pack4(col[0], col[TLD], col[2 * TLD], col[3 * TLD], e);   // rows past N are 0
+      }
+    }
+    if (layout == 1) {
+      uint8_t* dst = codes + ((bh * nt + t) * (int64_t)D + d) * 64 + 32 * j;
+      st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+      st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+      scales[((bh * nt + t) * 2 + j) * (int64_t)D + d] = sb;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) ctile[(32 * j + 4 * q + b) * D + d] = (uint8_t)(w[q] >> (8 * b));
+      if (cnt > 0) scales[(bh * nblk32 + 2 * t + j) * (int64_t)D + d] = sb;
+    }
+  }
+  if (layout == 0) {
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < 64 * (D / 16); ch += 256) {
+      const int r = ch / (D / 16), c = ch - r * (D / 16);
+      if (r0 + r < N)
+        st16(codes + (bh * N + r0 + r) * (int64_t)D + 16 * c, *(const u32x4*)&ctile[r * D + 16 * c]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MX attention: the quantised kernel's skeleton (4 waves x 32 query rows,
+// 64-key tiles, two workgroups per CU, code tiles by direct loads into
+// double buffers, one barrier per tile, S of tile i+1 beside the weights of
+// tile i) with the P V product in MX blocks:
+//   S_int^T = Kc Qc^T          i8 MFMA 32x32x32, exact int32; Q, K per-64-token
+//                               INT8 blocks (attn_quantize_qk)
+//   P^ = MX blocks of 32 keys of each query row, made in the kernel (scale
+//        2^E, E = floor(log2 block max) - 7: every element below 256)
+//   O^T += V^ P^T              v_mfma_scale_f32_32x32x64_f8f6f4 with V's and
+//                               P's E8M0 block scales as operands
+// so O accumulates in true units; the only rescale is the running-maximum one.
+//
+// Operand layout of the scaled FP8 MFMA (checked on the GPU): lane half h
+// holds k-slots 16 h + (0..15) in its bytes 0..15 and 32 + 16 h + (0..15) in
+// bytes 16..31; bytes 0..15 of both halves are scale block 0 (the scale comes
+// from lane half 0), bytes 16..31 block 1 (from lane half 1).
+template <typename TO, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float* __restrict__ qs,
+                  const int8_t* __restrict__ kc, const float* __restrict__ ks,
+                  const uint8_t* __restrict__ vct, const uint8_t* __restrict__ vs) {
+  constexpr int BM = 128;
+  constexpr int KS = D / 32;       // i8 k-steps (32 channels each)
+  constexpr int DB = D / 32;       // 32-channel blocks of O^T
+  constexpr int KCPR = D / 16;     // 16-byte chunks per K code row
+  constexpr int KRPI = 64 / KCPR;  // K rows per direct-load instruction
+  constexpr float kLag = 2.0f;     // the running maximum may trail by this (log2)
+  constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
+  __shared__ __attribute__((aligned(16))) uint8_t sk[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t svs[2][2 * D];   // V scales [block][channel]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / ntq, qt_in = tile - bh * ntq;
+  const int qt = a.causal ? ntq - 1 - qt_in : qt_in;   // heaviest causal q-tiles first
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int g = h / (a.Hq / a.Hkv);
+  const int bg = b * a.Hkv + g;
+  const int q0 = qt * BM;
+  const int nkt = (a.Nk + 63) / 64;
+  const int8_t* Qc = qc + (int64_t)bh * a.Nq * D;
+  const int8_t* Kc = kc + (int64_t)bg * a.Nk * D;
+  const float* Ks = ks + (int64_t)bg * nkt;
+  const uint8_t* Vt = vct + (int64_t)bg * nkt * D * 64;
+  const uint8_t* Vs = vs + (int64_t)bg * nkt * 2 * D;
+  TO* Op = (TO*)a.o + (int64_t)bh * a.Nq * D;
+
+  const int qlast = min(q0 + BM, a.Nq) - 1;
+  const int kv_lo = a.window_w > 0 ? max(a.window_lo, a.pos0 + q0 - a.window_w + 1) : a.window_lo;
+  const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
+  const int t_lo = kv_lo / 64;
+  const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
+
+  const int qrow = q0 + wave * 32 + col;
+  const int qw0 = q0 + wave * 32;
+  // Row qrow sees keys [row_lo, row_hi]; tiles inside the bounds common to
+  // the wave's rows, [wave_lo, wave_hi], are not masked.
+  const int wrow = a.window_w > 0 ? a.pos0 - a.window_w + 1 : -(1 << 30);
+  const int row_lo = max(kv_lo, qrow + wrow);
+  const int row_hi = a.causal ? min(a.pos0 + qrow, a.Nk - 1) : a.Nk - 1;
+  const int wave_lo = max(kv_lo, qw0 + 31 + wrow);
+  const int wave_hi = a.causal ? min(a.pos0 + qw0, a.Nk - 1) : a.Nk - 1;
+
+  // Q codes as B operands of the i8 MFMA: lane half h of k-step k holds
+  // channels 32 k + 16 h + (0..15); the wave's rows share one 64-row block.
+  i32x4 qv[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    u32x4 raw = {0, 0, 0, 0};
+    if (qrow < a.Nq) raw = ld16(Qc + (int64_t)qrow * D + 32 * k + 16 * half);
+    qv[k] = __builtin_bit_cast(i32x4, raw);
+  }
+  const float cq = qs[(int64_t)bh * ((a.Nq + 63) / 64) + min(qw0, a.Nq - 1) / 64] * a.c;
+
+  // K code row r holds key 32 blk + 16 h + 4 a + c for r = 32 blk + 8 a + 4 h + c:
+  // lane half h's scores of 32-key block blk are keys 32 blk + 16 h + (0..15),
+  // the bytes of P^T that the scaled MFMA wants, and each 32-key block of a
+  // row is one scale block. Chunk c of a row sits at c ^ kswz(r), chunk c of
+  // V^T row d at c ^ vswz(d).
+  auto kswz = [](int r) { return KCPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
+  auto vswz = [](int d) { return (d >> 2) & 3; };
+  auto kperm = [](int r) { return 32 * (r >> 5) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3); };
+  constexpr int NK = 16 / KRPI, NV = D / 64;
+  uint32_t kofs[NK], vofs[NV];
+#pragma unroll
+  for (int u = 0; u < NK; ++u) {
+    const int r = 16 * wave + KRPI * u + lane / KCPR, pos = lane % KCPR;
+    kofs[u] = (uint32_t)(kperm(r) * D + 16 * (pos ^ kswz(r)));
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int d = (D / 4) * wave + 16 * u + lane / 4, pos = lane % 4;
+    vofs[u] = (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
+  }
+  constexpr int NVS = 2 * D / 16;   // 16-byte pieces of a V scale tile
+  auto load_k = [&](int t, int buf) {
+    const int8_t* base = Kc + (int64_t)64 * t * D;
+    const int last = a.Nk - 1 - 64 * t;
+    if (last >= 63) {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) load_to_lds16(base, kofs[u], &sk[buf][(16 * wave + KRPI * u) * D]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int r0 = 16 * wave + KRPI * u;
+        const int r = r0 + lane / KCPR, pos = lane % KCPR;
+        load_to_lds16(base, (uint32_t)(min(kperm(r), last) * D + 16 * (pos ^ kswz(r))), &sk[buf][r0 * D]);
+      }
+    }
+  };
+  auto load_v = [&](int t, int buf) {
+    const uint8_t* base = Vt + (int64_t)t * D * 64;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) load_to_lds16(base, vofs[u], &sv[buf][((D / 4) * wave + 16 * u) * 64]);
+    // the tile's 2 D scale bytes ride along (wave 1)
+    if (wave == 1 && lane < NVS) load_to_lds16(Vs + (int64_t)t * 2 * D, (uint32_t)(16 * lane), &svs[buf][0]);
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // The int32 scores start from 0x4B400000, the bit pattern of 1.5 * 2^23:
+  // |S| < 2^22, so each accumulator read as a float is exactly 1.5 * 2^23 + S.
+  i32x16 magic;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) magic[j] = 0x4B400000;
+  asm volatile("" : "+v"(magic));
+  auto s_mma = [&](int buf, i32x16 (&s)[2]) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + col;
+        const i32x4 ka = *(const i32x4*)&sk[buf][r * D + 16 * ((2 * k + half) ^ kswz(r))];
+        s[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qv[k], k == 0 ? magic : s[mb], 0, 0, 0);
+      }
+  };
+
+  auto step = [&](int i, i32x16 (&cur)[2], i32x16 (&nxt)[2]) {
+    const int t = t_lo + i;
+    if (i + 2 < nt) load_k(t + 2, i & 1);
+    if (i + 1 < nt) load_v(t + 1, (i + 1) & 1);
+    // A block of zero codes has scale 0; the floor keeps masked scores at
+    // -inf (-inf * 0 would be NaN) and changes nothing else.
+    const float cf = fmaxf(cq * Ks[t], 1.17549435e-38f);
+    float sf[2][16];   // kOff + S, exact
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sf[mb][j] = __builtin_bit_cast(f32x16, cur[mb])[j];
+    const int k0 = 64 * t;
+    if (k0 < wave_lo || k0 + 63 > wave_hi) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * mb + 16 * half + 4 * (j >> 2) + (j & 3);
+          if (key < row_lo || key > row_hi) sf[mb][j] = -INFINITY;
+        }
+    }
+    float bm[2];   // per 32-key block: the lane's largest kOff + S
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      bm[mb] = sf[mb][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) bm[mb] = fmaxf(bm[mb], sf[mb][j]);
+      bm[mb] = halves_max(bm[mb]);
+    }
+    const float mx = (fmaxf(bm[0], bm[1]) - kOff) * cf;   // exact subtraction
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLag)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      m_run = m_new;
+    }
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
+    // exponent = S cf - mu = (kOff + S) cf - (kOff cf + mu): one FMA per
+    // score; the rounding of kOff cf + mu (< 0.9 cf + 2^-21) is far below the
+    // INT8 rounding of the scores for cf < 0.03, larger factors take the
+    // exact form.
+    float C = fmaf(kOff, cf, mu);
+    if (cf >= 0.03f) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sf[mb][j] -= kOff;
+        bm[mb] -= kOff;
+      }
+      C = mu;
+    }
+    // Each 32-key block mb of a row's weights (16 in each lane half) is one
+    // MX block with scale 2^E, E = floor(log2 of its largest weight) - 7, so
+    // its elements lie below 256. The largest weight's exponent is the block
+    // maximum through the same FMA, and 2^-E folds into the FMA's constant:
+    // the weights come out already scaled.
+    int E[2];
+    float Cm[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float x = fmaf(bm[mb], cf, -C);
+      E[mb] = bm[mb] == -INFINITY ? -127 : max((int)__builtin_floorf(x) - 7, -127);
+      Cm[mb] = C + (float)E[mb];   // exact: C's ulp is below 1 and E an integer
+    }
+
+    // S of tile i + 1 beside the weights of tile i.
+    s_mma((i + 1) & 1, nxt);
+    float ls[2] = {0.0f, 0.0f};
+    i32x8 pb;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -Cm[mb]));
+          ls[mb] += e[k];
+        }
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
+        pb[4 * mb + q4] = pk;
+      }
+    // the denominator takes the weights back to their unscaled values
+    l_run += __builtin_amdgcn_ldexpf(ls[0], E[0]) + __builtin_amdgcn_ldexpf(ls[1], E[1]);
+    const int psc = (half ? E[1] : E[0]) + 127;   // lane half h: scale of block h
+
+    // O^T += V^T P^T for tile i: one scaled FP8 MFMA per 32 channels (a
+    // scheduling fence keeps the V operand reads from being hoisted above
+    // the weights, which would run the wave out of registers).
+    __builtin_amdgcn_sched_barrier(0);
+    const int vb = i & 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = 32 * db + col;
+      const uint8_t* row = &sv[vb][d * 64];
+      const u32x4 lo = ld16(row + 16 * (half ^ vswz(d)));         // keys 16 h + (0..15)
+      const u32x4 hi = ld16(row + 16 * ((2 + half) ^ vswz(d)));   // keys 32 + 16 h + (0..15)
+      const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int vsc = svs[vb][half * D + d];
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, vsc, 0, psc);
+    }
+    vmem_wait_all();
+    __syncthreads();
+  };
+
+  if (nt > 0) {
+    load_k(t_lo, 0);
+    load_v(t_lo, 0);
+    if (nt > 1) load_k(t_lo + 1, 1);
+    vmem_wait_all();
+    __syncthreads();
+    i32x16 s0[2], s1[2];
+    s_mma(0, s0);
+    __syncthreads();   // step 0 overwrites the K buffer just read
+    int i = 0;
+    for (; i + 1 < nt; i += 2) {
+      step(i, s0, s1);
+      step(i + 1, s1, s0);
+    }
+    if (i < nt) step(i, s0, s1);
+  }
+
+  const float l = halves_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qrow < a.Nq) {
+    TO* orow = Op + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * db + 8 * a4 + 4 * half;
+        TO o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][4 * a4 + r] * inv);
+        *(u32x2*)(orow + d) = *(const u32x2*)o4;
+      }
+  }
+}
+
+template <typename TO, int D>
+hipError_t prefill_mx_t(const FwdArgs& a, const int8_t* qc, const float* qs, const int8_t* kc,
+                        const float* ks, const uint8_t* vct, const uint8_t* vs, hipStream_t st) {
+  const int ntq = (a.Nq + 127) / 128;
+  const int64_t grid = (int64_t)a.B * a.Hq * ntq;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_mx_kernel<TO, D>), dim3((unsigned)grid), dim3(256), 0, st, a, ntq,
+                     qc, qs, kc, ks, vct, vs);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t quant_mx_t(const void* x, int64_t BH, int N, int D, int axis, int layout, int srows,
+                      uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  if (axis == 0) {
+    const int64_t blocks = (BH * N * (D / 32) + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (D == 64)
+      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 64>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (const T*)x, BH, N, srows, codes, scales);
+    else
+      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 128>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (const T*)x, BH, N, srows, codes, scales);
+  } else {
+    const int64_t grid = BH * ((N + 63) / 64);
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (D == 64)
+      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st,
+                         (const T*)x, N, codes, scales, layout);
+    else
+      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st,
+                         (const T*)x, N, codes, scales, layout);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx(const void* x, int elem, int64_t BH, int N, int D, int axis, int layout,
+                           int srows, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  return elem == 2 ? quant_mx_t<__bf16>(x, BH, N, D, axis, layout, srows, codes, scales, s)
+                   : quant_mx_t<_Float16>(x, BH, N, D, axis, layout, srows, codes, scales, s);
+}
+
+hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs,
+                             const int8_t* kc, const float* ks, const uint8_t* vct,
+                             const uint8_t* vs, int elem_out, hipStream_t s) {
+  if (elem_out == 2)
+    return a.D == 64 ? prefill_mx_t<__bf16, 64>(a, qc, qs, kc, ks, vct, vs, s)
+                     : prefill_mx_t<__bf16, 128>(a, qc, qs, kc, ks, vct, vs, s);
+  return a.D == 64 ? prefill_mx_t<_Float16, 64>(a, qc, qs, kc, ks, vct, vs, s)
+                   : prefill_mx_t<_Float16, 128>(a, qc, qs, kc, ks, vct, vs, s);
+}
+
+}  // namespace attn

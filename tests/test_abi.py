@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
-              "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes",
+              "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
               "attn_status_string"):
         assert n in names
 
@@ -200,3 +200,20 @@ def test_sliding_workspace_bytes(lib):
     assert ws(1, 40, 40, 32760, 32760, 128, 1, 4096, 0, 0, 2) == 0      # bf16 prefill: none
     assert ws(1, 16, 8, 4, 4096, 128, 1, 1000, 4092, 0, 1) > 0          # decode partials
     assert ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0, 1) == 0            # window 0 rejected
+
+
+
+def test_mx_entry_points_reject_before_enqueue(lib):
+    q = lib.attn_quantize_mx
+    assert q(None, FAKE, FAKE, 1, 2, 64, 128, 0, 2, None) == E_INVALID
+    assert q(FAKE, FAKE, FAKE, 1, 2, 64, 96, 0, 2, None) == E_UNSUPPORTED     # D 96
+    assert q(FAKE, FAKE, FAKE, 1, 2, 64, 128, 0, 0, None) == E_UNSUPPORTED    # fp32
+    assert q(FAKE, FAKE, FAKE, 1, 2, 64, 128, 2, 2, None) == E_INVALID        # axis 2
+    assert q(FAKE + 4, FAKE, FAKE, 1, 2, 64, 128, 1, 2, None) == E_INVALID    # misaligned
+    # the MX mode of attn_fwd: 16-bit inputs only, and a workspace
+    assert _fwd(lib, mode=2, dtype=0) == E_UNSUPPORTED
+    assert _fwd(lib, mode=2) == E_WORKSPACE
+    ws = lib.attn_fwd_workspace_bytes
+    need = ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 2, 2)
+    # codes of Q, K, V (1 byte each) plus scale bytes (one per 32 elements, K and V padded)
+    assert need >= 3 * 40 * 32760 * 128 + 3 * 40 * 32760 * 128 // 32
