@@ -215,5 +215,6 @@ def test_mx_entry_points_reject_before_enqueue(lib):
     assert _fwd(lib, mode=2) == E_WORKSPACE
     ws = lib.attn_fwd_workspace_bytes
     need = ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 2, 2)
-    # codes of Q, K, V (1 byte each) plus scale bytes (one per 32 elements, K and V padded)
-    assert need >= 3 * 40 * 32760 * 128 + 3 * 40 * 32760 * 128 // 32
+    # INT8 codes of Q and K, E4M3 codes of V (1 byte each), V's scale bytes (one
+    # per 32 keys of a channel) and the fp32 scales of Q's and K's 64-token blocks
+    assert need >= 3 * 40 * 32760 * 128 + 40 * 32760 * 128 // 32 + 2 * 40 * 512 * 4
