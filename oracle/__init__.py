@@ -15,6 +15,8 @@ the definitions and the passages they follow):
 * :func:`attn_kvq` — exact attention over a quantised KV cache (codes + scales).
 * :func:`quant_mx` — OCP MX FP8 blocks (32 E4M3 elements, one E8M0 scale).
 * :func:`attn_mx` — exact attention on the MX variant's inputs (INT8 Q, K; MX V).
+* :func:`rope_freqs`, :func:`rope_apply`, :func:`attn_rope` — rotary position
+  embedding (plain, NTK, YaRN) and attention on rotated Q, K.
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and library special cases. ``attn_quant`` is
@@ -71,6 +73,13 @@ def _load():
         lib.oracle_quant_mx.restype = i
         lib.oracle_attn_mx.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d, vp, i64, vp, i]
         lib.oracle_attn_mx.restype = i
+        lib.oracle_rope_freqs.argtypes = [i, i, d, d, i, d, d, vp, vp]
+        lib.oracle_rope_freqs.restype = i
+        lib.oracle_rope_apply.argtypes = [vp, i, i64, i, i, i, i, vp, vp]
+        lib.oracle_rope_apply.restype = i
+        lib.oracle_attn_rope.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d,
+                                         i, i, d, d, i, d, d, vp, i64, vp, i]
+        lib.oracle_attn_rope.restype = i
         lib.oracle_quant_int8.argtypes = [vp, i, i64, i, i, vp, vp]
         lib.oracle_quant_int8.restype = i
         lib.oracle_quant_e4m3.argtypes = [vp, i, i64, i, i, vp, vp]
@@ -230,6 +239,61 @@ def attn_mx(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None, nth
         nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_attn_mx rejected the arguments")
+    return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+
+
+def rope_freqs(D, scaling=ROPE_PLAIN, base=10000.0, factor=1.0, orig_ctx=4096,
+               beta_fast=32.0, beta_slow=1.0):
+    """Rotary frequencies theta [D/2] (float64) and the logit multiplier."""
+    theta = np.zeros(D // 2, dtype=np.float64)
+    mult = np.zeros(1, dtype=np.float64)
+    rc = _load().oracle_rope_freqs(D, scaling, float(base), float(factor), int(orig_ctx),
+                                   float(beta_fast), float(beta_slow), theta.ctypes.data,
+                                   mult.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_rope_freqs rejected the arguments")
+    return theta, float(mult[0])
+
+
+def rope_apply(x, pos_base, theta, style=ROPE_HALF):
+    """x [..., N, D] rotated at positions pos_base + n: float64 numpy."""
+    x = _cpu(x)
+    *lead, N, D = x.shape
+    BH = int(np.prod(lead)) if lead else 1
+    out = np.zeros(x.shape, dtype=np.float64)
+    th = np.ascontiguousarray(np.asarray(theta, dtype=np.float64))
+    rc = _load().oracle_rope_apply(x.data_ptr(), DTYPE_CODE[x.dtype], BH, N, D, int(pos_base),
+                                   int(style), th.ctypes.data, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_rope_apply rejected the arguments")
+    return out
+
+
+def attn_rope(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, style=ROPE_HALF,
+              scaling=ROPE_PLAIN, base=10000.0, factor=1.0, orig_ctx=4096, beta_fast=32.0,
+              beta_slow=1.0, rows=None, nthreads=None):
+    """Exact fp64 attention on Q rotated at positions pos0 + i and K at j."""
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if rows is None:
+        nrows, rows_arr = B * Hq * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_attn_rope(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), float(scale),
+        int(style), int(scaling), float(base), float(factor), int(orig_ctx), float(beta_fast),
+        float(beta_slow), None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        out.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_rope rejected the arguments")
     return out.reshape(B, Hq, Nq, D) if rows is None else out
 
 

@@ -35,6 +35,9 @@
  *                       sharing one power-of-two (E8M0) scale, along D or N.
  *   oracle_attn_mx      exact attention on the MX variant's inputs: INT8
  *                       Q, K blocks and V in MX blocks along the keys.
+ *   oracle_rope_freqs   rotary frequencies: plain, NTK-aware, YaRN.
+ *   oracle_rope_apply   the rotation of Q or K rows at their positions.
+ *   oracle_attn_rope    exact attention on rotated Q and K.
  *
  * Readings taken where the pages are silent (listed again in the design
  * notes): query row i sits at absolute position pos0 + i and key j at j; a
@@ -49,6 +52,9 @@
  *        -pthread oracle.c -o liboracle.so -lm
  * (no contraction: the fp32 quantiser arithmetic must round after every op).
  */
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -527,6 +533,114 @@ int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
     rc = run_attn(&J, nthreads);
   }
   free(qh); free(kh); free(vh);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ RoPE -- */
+
+/*
+ * Rotary position embedding, the "RoPE with NTK / YaRN scaling inside the
+ * kernel" of section "Plans" of "Attention kernels on a home RTX 5080". The
+ * page gives no formulas; the published definitions are followed.
+ *   plain  theta_i = base^(-2 i / D), i = 0 .. D/2 - 1 (RoFormer);
+ *   NTK    the same with base * s^(D / (D - 2)) (NTK-aware scaling, factor s);
+ *   YaRN   theta_i' = (1 - g_i) theta_i / s + g_i theta_i, with
+ *          g_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1) and
+ *          r_i = L theta_i / (2 pi) (the original context L over the
+ *          wavelength), and the logits multiplied by (0.1 ln s + 1)^2.
+ * scaling: 0 plain, 1 NTK, 2 YaRN. theta: D/2 doubles; *logit_mult: 1 unless
+ * YaRN.
+ */
+int oracle_rope_freqs(int D, int scaling, double base, double factor, int orig_ctx,
+                      double beta_fast, double beta_slow, double* theta, double* logit_mult) {
+  if (D < 2 || D % 2 != 0 || !(base > 0.0) || scaling < 0 || scaling > 2) return -1;
+  if (scaling != 0 && !(factor >= 1.0)) return -1;
+  if (scaling == 2 && (orig_ctx < 1 || !(beta_fast > beta_slow))) return -1;
+  double b = base;
+  if (scaling == 1) b = base * pow(factor, (double)D / (double)(D - 2));
+  for (int i = 0; i < D / 2; ++i) {
+    double t = pow(b, -2.0 * i / (double)D);
+    if (scaling == 2) {
+      double r = (double)orig_ctx * t / (2.0 * M_PI);
+      double g = (r - beta_slow) / (beta_fast - beta_slow);
+      if (g < 0.0) g = 0.0;
+      if (g > 1.0) g = 1.0;
+      t = (1.0 - g) * t / factor + g * t;
+    }
+    theta[i] = t;
+  }
+  *logit_mult = 1.0;
+  if (scaling == 2) {
+    double m = 0.1 * log(factor) + 1.0;
+    *logit_mult = m * m;
+  }
+  return 0;
+}
+
+/*
+ * Rotate rows of x ([BH][N][D], element type dtype) into out (doubles): row n
+ * of every head sits at position pos_base + n; pair i is (x_i, x_{i + D/2})
+ * for style 0 (half-split) or (x_{2i}, x_{2i+1}) for style 1 (interleaved),
+ * (a, b) -> (a cos(p theta_i) - b sin(p theta_i), a sin(p theta_i) + b cos(p theta_i)).
+ */
+int oracle_rope_apply(const void* x, int dtype, int64_t BH, int N, int D, int pos_base, int style,
+                      const double* theta, double* out) {
+  if (BH < 1 || N < 1 || D < 2 || D % 2 != 0 || (style != 0 && style != 1)) return -1;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int n = 0; n < N; ++n) {
+      int64_t base = (bh * N + n) * (int64_t)D;
+      double pos = (double)pos_base + n;
+      for (int i = 0; i < D / 2; ++i) {
+        int ia = style == 0 ? i : 2 * i;
+        int ib = style == 0 ? i + D / 2 : 2 * i + 1;
+        double a = load_elem(x, dtype, base + ia), b = load_elem(x, dtype, base + ib);
+        double c = cos(pos * theta[i]), s = sin(pos * theta[i]);
+        out[base + ia] = a * c - b * s;
+        out[base + ib] = a * s + b * c;
+      }
+    }
+  return 0;
+}
+
+/*
+ * Exact attention (arguments and conventions of oracle_attn, no per-row
+ * window) on Q rotated at positions pos0 + i and K at positions j, with the
+ * scale multiplied by the YaRN logit factor.
+ */
+int oracle_attn_rope(const void* q, const void* k, const void* v, int dtype,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                     int causal, int window_lo, int pos0, double scale,
+                     int style, int scaling, double base, double factor, int orig_ctx,
+                     double beta_fast, double beta_slow,
+                     const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  double* theta = (double*)malloc(sizeof(double) * (size_t)(D / 2 > 0 ? D / 2 : 1));
+  double mult = 1.0;
+  if (!theta || oracle_rope_freqs(D, scaling, base, factor, orig_ctx, beta_fast, beta_slow,
+                                  theta, &mult) != 0) {
+    free(theta);
+    return -1;
+  }
+  int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+  double* qh = (double*)malloc(sizeof(double) * (size_t)nq);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)nk);
+  int rc = -1;
+  if (qh && kh &&
+      oracle_rope_apply(q, dtype, (int64_t)B * Hq, Nq, D, pos0, style, theta, qh) == 0 &&
+      oracle_rope_apply(k, dtype, (int64_t)B * Hkv, Nk, D, 0, style, theta, kh) == 0) {
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+    J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.scale = scale * mult;
+    J.rows = rows;
+    J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+    J.out = out;
+    J.qhat = qh; J.khat = kh;
+    rc = run_attn(&J, nthreads);
+  }
+  free(theta); free(qh); free(kh);
   return rc;
 }
 
