@@ -112,6 +112,60 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                 int mode, int dtype);
 
 /*
+ * Rotary position embedding (RoPE) of Q and K, the "RoPE with NTK / YaRN
+ * scaling inside the kernel" of section "Plans" of "Attention kernels on a
+ * home RTX 5080" (the page gives no formulas; the published ones are used).
+ * Query row i sits at position pos0 + i, key j at position j. Pair i of a row
+ * (i = 0 .. D/2 - 1) turns by the angle position * theta_i:
+ *   (a, b) -> (a cos - b sin, a sin + b cos).
+ */
+typedef enum {
+  ATTN_ROPE_HALF = 0,        /* pairs (x_i, x_{i + D/2}) */
+  ATTN_ROPE_INTERLEAVED = 1  /* pairs (x_{2i}, x_{2i+1}) */
+} attn_rope_style;
+
+typedef enum {
+  ATTN_ROPE_PLAIN = 0,  /* theta_i = base^(-2i/D) */
+  ATTN_ROPE_NTK = 1,    /* the same with base * factor^(D / (D - 2)) */
+  ATTN_ROPE_YARN = 2    /* theta_i' = (1 - g_i) theta_i / factor + g_i theta_i with
+                           g_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1),
+                           r_i = orig_ctx * theta_i / (2 pi); logits (scale) multiplied
+                           by (0.1 ln factor + 1)^2 */
+} attn_rope_scaling;
+
+typedef struct {
+  int style;        /* attn_rope_style */
+  int scaling;      /* attn_rope_scaling */
+  float base;       /* finite, > 0 (e.g. 10000) */
+  float factor;     /* finite, >= 1 (NTK, YaRN) */
+  int orig_ctx;     /* >= 1 (YaRN): the context the frequencies were trained on */
+  float beta_fast;  /* YaRN ramp: beta_fast > beta_slow (e.g. 32 and 1) */
+  float beta_slow;
+} attn_rope;
+
+/*
+ * attn_fwd_rope — attn_fwd on rotary-embedded Q and K: the result is
+ * attention on RoPE(Q) and RoPE(K) (same arguments, layouts, modes and error
+ * behaviour as attn_fwd; `rope` NULL gives attn_fwd itself; invalid rope
+ * fields give ATTN_E_INVALID). The kernels turn Q in registers as they load
+ * it (once per workgroup); K is turned once per call: inside the INT8
+ * quantiser in the quantised and MX modes, by one pass into the workspace in
+ * the exact mode (a kernel that turned K on every load would redo it for
+ * every query tile).
+ *   workspace  at least attn_fwd_rope_workspace_bytes(...) bytes.
+ */
+int attn_fwd_rope(const void* q, const void* k, const void* v, void* o,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                  int causal, int window_lo, int pos0, float scale, int mode, int dtype,
+                  const attn_rope* rope, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Workspace attn_fwd_rope needs (host-only; 0 for rejected arguments). */
+size_t attn_fwd_rope_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                     int causal, int window_lo, int pos0, int mode,
+                                     int dtype);
+
+/*
  * attn_fwd_sliding — attn_fwd with a per-row sliding window instead of the
  * shared lower bound: query row i (absolute position pos0 + i) sees key j
  * only if j >= pos0 + i - window + 1, and, when causal, j <= pos0 + i; so a

@@ -16,6 +16,8 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_bytes",
+           "fwd_rope", "fwd_rope_workspace_bytes", "Rope", "ROPE_HALF", "ROPE_INTERLEAVED",
+           "ROPE_PLAIN", "ROPE_NTK", "ROPE_YARN",
            "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
            "decode_kvq_workspace_bytes", "load_library",
            "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
@@ -26,6 +28,19 @@ MODE_EXACT = 0
 MODE_QUANT = 1
 MODE_MX = 2
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2
+
+
+class Rope(ctypes.Structure):
+    """attn_rope of include/attn.h: rotary position embedding of Q and K."""
+    _fields_ = [("style", ctypes.c_int), ("scaling", ctypes.c_int), ("base", ctypes.c_float),
+                ("factor", ctypes.c_float), ("orig_ctx", ctypes.c_int),
+                ("beta_fast", ctypes.c_float), ("beta_slow", ctypes.c_float)]
+
+    def __init__(self, style=ROPE_HALF, scaling=ROPE_PLAIN, base=10000.0, factor=1.0,
+                 orig_ctx=4096, beta_fast=32.0, beta_slow=1.0):
+        super().__init__(style, scaling, base, factor, orig_ctx, beta_fast, beta_slow)
 
 _lib = None
 
@@ -51,6 +66,11 @@ def load_library():
     lib.attn_fwd_sliding.restype = i
     lib.attn_fwd_sliding_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
     lib.attn_fwd_sliding_workspace_bytes.restype = sz
+    lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i,
+                                  ctypes.POINTER(Rope), vp, sz, vp]
+    lib.attn_fwd_rope.restype = i
+    lib.attn_fwd_rope_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
+    lib.attn_fwd_rope_workspace_bytes.restype = sz
     lib.attn_quantize_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_quantize_qk.restype = i
     lib.attn_quantize_v.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
@@ -164,6 +184,32 @@ def fwd_sliding(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window, ca
                               float(scale), int(mode), _DTYPE[q.dtype], ws_ptr, ws_len,
                               _stream_handle(q))
     _check(st, "attn_fwd_sliding")
+    return out
+
+
+def fwd_rope_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos0=0,
+                             mode=MODE_EXACT, dtype=torch.bfloat16) -> int:
+    return int(load_library().attn_fwd_rope_workspace_bytes(
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), int(mode), _DTYPE[dtype]))
+
+
+def fwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope: Rope, *, causal=False,
+             window_lo=0, pos0=0, scale=None, mode=MODE_EXACT, out=None,
+             workspace=None) -> torch.Tensor:
+    """Attention on rotary-embedded Q (row i at position pos0 + i) and K (key j at j)."""
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fwd_rope_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal=causal, window_lo=window_lo,
+                                    pos0=pos0, mode=mode, dtype=q.dtype)
+    out, ws_ptr, ws_len = _out_and_workspace(q, out, workspace, need)
+    st = lib.attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo), int(pos0),
+                           float(scale), int(mode), _DTYPE[q.dtype],
+                           None if rope is None else ctypes.byref(rope), ws_ptr, ws_len,
+                           _stream_handle(q))
+    _check(st, "attn_fwd_rope")
     return out
 
 

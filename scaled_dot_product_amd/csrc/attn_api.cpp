@@ -4,6 +4,7 @@
 // no effect on the device.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/attn.h"
 #include "attn_internal.hpp"
@@ -70,6 +71,7 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, int B, i
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
   a.causal = causal ? 1 : 0; a.window_lo = window_lo; a.pos0 = pos0; a.window_w = 0;
+  memset(&a.rope, 0, sizeof a.rope);   // no rotation unless attn_fwd_rope sets it
   a.scale = scale;
   // Kept a normal float so that masked scores (-inf) times c stay -inf.
   a.c = fmaxf(scale * kLog2eHost, 1.17549435e-38f);
@@ -81,6 +83,7 @@ struct Layout {
   size_t bf16_q = 0, bf16_k = 0, bf16_v = 0;       // fp32 inputs rounded to bf16
   size_t qc = 0, qs = 0, kc = 0, ks = 0, vc = 0, vs = 0;  // quantised mode
   size_t dec = 0;                                  // decode partials
+  size_t rk = 0;                                   // rotated K (exact mode with RoPE)
   size_t total = 0;
   bool decode = false;
   DecodePlan plan{};
@@ -117,6 +120,8 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
     L.bf16_q = off; off = round_up(off + nq * 2);
     L.bf16_k = off; off = round_up(off + nk * 2);
     L.bf16_v = off; off = round_up(off + nk * 2);
+  } else if (a.rope.on) {
+    L.rk = off; off = round_up(off + nk * 2);   // fp32 inputs rotate their bf16 copy in place
   }
   if (decode_eligible(a)) {
     L.decode = true;
@@ -125,6 +130,53 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
   }
   L.total = off;
   return L;
+}
+
+// Rotary frequencies of attn_rope (the published rules; double precision):
+// plain theta_i = base^(-2i/D); NTK: base * s^(D/(D-2)); YaRN: theta_i blended
+// between theta_i / s and theta_i by the ramp over L theta_i / (2 pi), logits
+// times (0.1 ln s + 1)^2. Stored as revolutions per position, hi + lo floats.
+int make_rope(const attn_rope* p, int D, RopeArgs* r, double* logit_mult) {
+  r->on = 0;
+  r->style = 0;
+  *logit_mult = 1.0;
+  if (!p) return ATTN_OK;
+  if (p->style != ATTN_ROPE_HALF && p->style != ATTN_ROPE_INTERLEAVED) return ATTN_E_INVALID;
+  if (p->scaling != ATTN_ROPE_PLAIN && p->scaling != ATTN_ROPE_NTK && p->scaling != ATTN_ROPE_YARN)
+    return ATTN_E_INVALID;
+  if (!isfinite(p->base) || !(p->base > 0.0f)) return ATTN_E_INVALID;
+  if (p->scaling != ATTN_ROPE_PLAIN && (!isfinite(p->factor) || !(p->factor >= 1.0f)))
+    return ATTN_E_INVALID;
+  if (p->scaling == ATTN_ROPE_YARN &&
+      (p->orig_ctx < 1 || !isfinite(p->beta_fast) || !isfinite(p->beta_slow) ||
+       !(p->beta_fast > p->beta_slow)))
+    return ATTN_E_INVALID;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double s = p->factor;
+  double b = p->base;
+  if (p->scaling == ATTN_ROPE_NTK) b = p->base * pow(s, (double)D / (double)(D - 2));
+  for (int i = 0; i < kRopeMaxPairs; ++i) {
+    double theta = 0.0;
+    if (i < D / 2) {
+      theta = pow(b, -2.0 * i / (double)D);
+      if (p->scaling == ATTN_ROPE_YARN) {
+        const double ratio = (double)p->orig_ctx * theta / two_pi;   // context over wavelength
+        double g = (ratio - p->beta_slow) / ((double)p->beta_fast - p->beta_slow);
+        g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+        theta = (1.0 - g) * theta / s + g * theta;
+      }
+    }
+    const double rev = theta / two_pi;
+    r->rev_hi[i] = (float)rev;
+    r->rev_lo[i] = (float)(rev - (double)r->rev_hi[i]);
+  }
+  if (p->scaling == ATTN_ROPE_YARN) {
+    const double m = 0.1 * log(s) + 1.0;
+    *logit_mult = m * m;
+  }
+  r->on = 1;
+  r->style = p->style;
+  return ATTN_OK;
 }
 
 // One validated forward call: workspace check and kernel dispatch.
@@ -141,13 +193,14 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   char* ws = (char*)workspace;
   hipError_t e = hipSuccess;
 
+  const RopeArgs* rope = a.rope.on ? &a.rope : nullptr;   // fused into the INT8 quantiser
   if (mode == ATTN_MODE_MX) {
     const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
     e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
-                          (float*)(ws + L.qs), s);
+                          (float*)(ws + L.qs), s, rope, a.pos0);
     if (e == hipSuccess)
       e = launch_quant_int8(k, elem, (int64_t)B * Hkv, Nk, D, (int8_t*)(ws + L.kc),
-                            (float*)(ws + L.ks), s);
+                            (float*)(ws + L.ks), s, rope, 0);
     if (e == hipSuccess)
       e = launch_quant_mx(v, elem, (int64_t)B * Hkv, Nk, D, 1, 1, 0, (uint8_t*)(ws + L.vc),
                           (uint8_t*)(ws + L.vs), s);
@@ -160,10 +213,10 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   if (mode == ATTN_MODE_QUANT) {
     const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
     e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
-                          (float*)(ws + L.qs), s);
+                          (float*)(ws + L.qs), s, rope, a.pos0);
     if (e == hipSuccess)
       e = launch_quant_int8(k, elem, (int64_t)B * Hkv, Nk, D, (int8_t*)(ws + L.kc),
-                            (float*)(ws + L.ks), s);
+                            (float*)(ws + L.ks), s, rope, 0);
     if (e == hipSuccess)
       e = launch_quant_e4m3(v, elem, (int64_t)B * Hkv, Nk, D, (uint8_t*)(ws + L.vc),
                             (float*)(ws + L.vs), 1, s);
@@ -185,6 +238,13 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
     a.q = ws + L.bf16_q;
     a.k = ws + L.bf16_k;
     a.v = ws + L.bf16_v;
+  }
+  if (a.rope.on) {
+    // K turned once per call, in one pass (the kernels turn Q themselves)
+    void* dst = out_f32 ? (void*)(ws + L.bf16_k) : (void*)(ws + L.rk);
+    e = launch_rope(a.k, dst, elem, (int64_t)B * Hkv, Nk, D, 0, a.rope, s);
+    if (e != hipSuccess) return ATTN_E_HIP;
+    a.k = dst;
   }
   if (L.decode)
     e = launch_decode(a, L.plan, elem, out_f32, ws + L.dec, s);
@@ -217,6 +277,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   if (!q || !k || !v || !o) return ATTN_E_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
   FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+  return fwd_dispatch(a, mode, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t attn_fwd_rope_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                                     int window_lo, int pos0, int mode, int dtype) {
+  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype) != ATTN_OK)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  a.rope.on = 1;
+  return plan_layout(a, mode, dtype).total;
+}
+
+int attn_fwd_rope(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                  int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale,
+                  int mode, int dtype, const attn_rope* rope, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+  double mult = 1.0;
+  st = make_rope(rope, D, &a.rope, &mult);
+  if (st != ATTN_OK) return st;
+  if (mult != 1.0) {
+    a.scale = (float)(scale * mult);
+    a.c = fmaxf(a.scale * kLog2eHost, 1.17549435e-38f);
+  }
   return fwd_dispatch(a, mode, dtype, workspace, workspace_bytes, stream);
 }
 

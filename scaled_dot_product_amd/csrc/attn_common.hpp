@@ -173,6 +173,58 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Rotary position embedding of one pair: (x, y) turns by the angle
+// 2 pi pos (rhi + rlo). The product pos * rhi is split exactly (FMA residual)
+// and reduced to its fraction before the hardware sine and cosine, which take
+// revolutions, so large positions keep their precision.
+__device__ __forceinline__ void rope_rotate(float& x, float& y, float pos, float rhi, float rlo) {
+  const float a = pos * rhi;
+  const float lo = fmaf(pos, rhi, -a) + pos * rlo;
+  const float f = (a - __builtin_rintf(a)) + lo;   // |f| <= 0.5 + 2^-20
+  const float c = __builtin_amdgcn_cosf(f), s = __builtin_amdgcn_sinf(f);
+  const float x2 = x * c - y * s;
+  y = x * s + y * c;
+  x = x2;
+}
+
+// Rotate the query row a lane holds as MFMA operands: KS vectors of 8
+// elements, vector ks holding channels 16 ks + 8 half + (0..7) (D = 16 KS).
+// style 0 pairs channel c with c + D/2 (vector ks with ks + KS/2, same lane);
+// style 1 pairs 2i with 2i + 1 (inside one vector). rh/rl: revolutions per
+// position of each pair, indexed by compile-time constants only.
+template <typename T, int KS>
+__device__ __forceinline__ void rope_lane_row(typename Elem<T>::vec8 (&v)[KS], float pos, int half,
+                                              int style, const float* rh, const float* rl) {
+  float x[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[ks][e] = (float)v[ks][e];
+  if (style == 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i0 = 16 * ks + e;
+        rope_rotate(x[ks][e], x[ks + KS / 2][e], pos, half ? rh[i0 + 8] : rh[i0],
+                    half ? rl[i0 + 8] : rl[i0]);
+      }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i0 = 8 * ks + u;
+        rope_rotate(x[ks][2 * u], x[ks][2 * u + 1], pos, half ? rh[i0 + 4] : rh[i0],
+                    half ? rl[i0 + 4] : rl[i0]);
+      }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[ks][e] = Elem<T>::from_float(x[ks][e]);
+}
+
 // Key index inside a 32-key block held by C-row m of S^T: swapping bits 2 and
 // 3 makes lane half h's registers j = 8t + i hold keys 16t + 8h + i, i.e. a
 // contiguous 8-key B-operand slice for each 16-key step of P V. It is its own

@@ -282,6 +282,9 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   V8 qv[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(V8, ld16(Qrow + 16 * ks + 8 * half));
+  // rotary position embedding of the row at position pos0 + qi (K arrives rotated)
+  if (a.rope.on)
+    rope_lane_row<T, KS>(qv, (float)(a.pos0 + qi), half, a.rope.style, a.rope.rev_hi, a.rope.rev_lo);
 
   // Tiles go straight into LDS (16 bytes per lane, 1 KB per instruction) with
   // the XOR chunk swizzles and K row order of the prefill: K row r holds key

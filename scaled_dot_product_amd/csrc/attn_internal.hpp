@@ -10,6 +10,16 @@ namespace attn {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Rotary position embedding of one call: pair i turns by 2 pi pos * rev_i
+// revolutions, rev_i = theta_i / (2 pi) held as the sum of two floats.
+constexpr int kRopeMaxPairs = 64;
+struct RopeArgs {
+  int on;      // 0: no rotation
+  int style;   // 0: pairs (c, c + D/2); 1: pairs (2i, 2i + 1)
+  float rev_hi[kRopeMaxPairs];
+  float rev_lo[kRopeMaxPairs];
+};
+
 // Arguments of one forward call after validation.
 struct FwdArgs {
   const void* q;
@@ -21,6 +31,7 @@ struct FwdArgs {
   int window_w;  // > 0: row i also needs key >= pos0 + i - window_w + 1
   float scale;
   float c;  // scale * log2(e): scores are exponentiated with exp2
+  RopeArgs rope;   // rotation of Q in the kernels (K is rotated before them)
 };
 
 // Visible key range [lo, hi) over all rows of a call (hi <= lo: none).
@@ -59,8 +70,13 @@ hipError_t launch_decode_kvq(const FwdArgs& a, const DecodePlan& p, const int8_t
 hipError_t launch_f32_to_bf16(const float* x, void* y, int64_t n, hipStream_t s);
 
 // ---- quantised mode ------------------------------------------------------
+// rope (optional): rotate each row at position pos_base + n before quantising.
 hipError_t launch_quant_int8(const void* x, int elem, int64_t BH, int N, int D,
-                             int8_t* codes, float* scales, hipStream_t s);
+                             int8_t* codes, float* scales, hipStream_t s,
+                             const RopeArgs* rope = nullptr, int pos_base = 0);
+// Rows of x ([BH][N][D]) rotated at positions pos_base + n into y (may be x).
+hipError_t launch_rope(const void* x, void* y, int elem, int64_t BH, int N, int D, int pos_base,
+                       const RopeArgs& rope, hipStream_t s);
 // layout 0: codes [BH][N][D]; layout 1: per 64-key tile, transposed
 // [BH][ceil(N/64)][D][64] with zero codes for keys past N.
 hipError_t launch_quant_e4m3(const void* x, int elem, int64_t BH, int N, int D,

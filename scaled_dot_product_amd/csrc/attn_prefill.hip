@@ -106,6 +106,10 @@ prefill_kernel(FwdArgs a, int ntq) {
     if (qrow < a.Nq) raw = ld16(Qp + (int64_t)qrow * D + 16 * ks + 8 * half);
     qv[ks] = __builtin_bit_cast(V8, raw);
   }
+  // rotary position embedding of the row at position pos0 + qrow, once per
+  // workgroup in registers (K arrives rotated)
+  if (a.rope.on)
+    rope_lane_row<T, KS>(qv, (float)(a.pos0 + qrow), half, a.rope.style, a.rope.rev_hi, a.rope.rev_lo);
 
   // LDS tiles are 64 unpadded rows of D elements; chunk c of row r sits at
   // chunk position c ^ swz(r). K row r holds key (r & ~31) | swap23(r & 31)

@@ -39,13 +39,19 @@ __device__ __forceinline__ float block_amax(float v, float* red) {
 }
 
 // One workgroup per 64-token block of one head. Thread -> (token, chunk).
+// With rope.on, each row is first turned by its rotary position embedding at
+// position pos_base + n (the rotation fused into the pass that reads the
+// row anyway).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) quant_int8_kernel(const T* __restrict__ x, int N,
                                                           int8_t* __restrict__ codes,
-                                                          float* __restrict__ scales) {
+                                                          float* __restrict__ scales,
+                                                          RopeArgs rope, int pos_base) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per token row
   constexpr int PER = 64 * CPR / 256;        // chunks per thread
+  static_assert(256 % CPR == 0, "a thread keeps one chunk position");
   __shared__ float red[4];
+  __shared__ float rh[kRopeMaxPairs], rl[kRopeMaxPairs];
   const int nblk = (N + 63) / 64;
   const int64_t bh = blockIdx.x / nblk;
   const int t = blockIdx.x - (int)(bh * nblk);
@@ -64,9 +70,43 @@ __global__ void __launch_bounds__(256) quant_int8_kernel(const T* __restrict__ x
     u32x4 raw = {0, 0, 0, 0};
     if (live[u]) raw = ld16(src + (int64_t)row * D + 8 * c);
     unpack8<T>(raw, vals[u]);
+  }
+  if (rope.on) {
+    if (threadIdx.x < kRopeMaxPairs) {
+      rh[threadIdx.x] = rope.rev_hi[threadIdx.x];
+      rl[threadIdx.x] = rope.rev_lo[threadIdx.x];
+    }
+    __syncthreads();
+    const int c = threadIdx.x % CPR;         // the same chunk position for every u
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const float pos = (float)(pos_base + r0 + (int)((threadIdx.x + 256 * u) / CPR));
+      if (rope.style == 0) {
+        // channel 8 c + e pairs with the one D/2 away: chunk c ^ (CPR/2), the
+        // same row in lane ^ (CPR/2) of this wave
+        constexpr int HP = CPR / 2;
+        const bool first = c < HP;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float other = __shfl_xor(vals[u][e], HP, 64);
+          const int i = (c % HP) * 8 + e;
+          float xa = first ? vals[u][e] : other, xb = first ? other : vals[u][e];
+          rope_rotate(xa, xb, pos, rh[i], rl[i]);
+          vals[u][e] = first ? xa : xb;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 4 * c + q;
+          rope_rotate(vals[u][2 * q], vals[u][2 * q + 1], pos, rh[i], rl[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(vals[u][i]));
-  }
   amax = block_amax(amax, red);
   float inv = 0.0f;
   if (amax > 0.0f) inv = 127.0f / amax;   // correctly rounded fp32 division
@@ -474,13 +514,79 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 
 template <typename T>
 hipError_t quant_int8_t(const void* x, int64_t BH, int N, int D, int8_t* c, float* s,
-                        hipStream_t st) {
+                        hipStream_t st, const RopeArgs& rope, int pos_base) {
   const int64_t grid = BH * ((N + 63) / 64);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (D == 64)
-    hipLaunchKernelGGL((quant_int8_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x, N, c, s);
+    hipLaunchKernelGGL((quant_int8_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x,
+                       N, c, s, rope, pos_base);
   else
-    hipLaunchKernelGGL((quant_int8_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x, N, c, s);
+    hipLaunchKernelGGL((quant_int8_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x,
+                       N, c, s, rope, pos_base);
+  return hipGetLastError();
+}
+
+// Rotary position embedding of whole rows (for K in the exact mode, one pass
+// in and out): row n of each head at position pos_base + n. Style 0: one
+// thread per (row, chunk c < CPR/2) turns chunks c and c + CPR/2 together;
+// style 1: one thread per (row, chunk). x and y may be the same buffer.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) rope_kernel(const T* x, T* y, int64_t nrows, int N,
+                                                   int pos_base, RopeArgs rope) {
+  constexpr int CPR = D / 8;
+  __shared__ float rh[kRopeMaxPairs], rl[kRopeMaxPairs];
+  if (threadIdx.x < kRopeMaxPairs) {
+    rh[threadIdx.x] = rope.rev_hi[threadIdx.x];
+    rl[threadIdx.x] = rope.rev_lo[threadIdx.x];
+  }
+  __syncthreads();
+  const int per_row = rope.style == 0 ? CPR / 2 : CPR;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nrows * per_row) return;
+  const int64_t row = id / per_row;
+  const int c = (int)(id - row * per_row);
+  const float pos = (float)(pos_base + (int)(row % N));
+  const T* src = x + row * D;
+  T* dst = y + row * D;
+  if (rope.style == 0) {
+    float a[8], b[8];
+    unpack8<T>(ld16(src + 8 * c), a);
+    unpack8<T>(ld16(src + 8 * (c + CPR / 2)), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_rotate(a[e], b[e], pos, rh[8 * c + e], rl[8 * c + e]);
+    T oa[8], ob[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      oa[e] = Elem<T>::from_float(a[e]);
+      ob[e] = Elem<T>::from_float(b[e]);
+    }
+    st16(dst + 8 * c, *(const u32x4*)oa);
+    st16(dst + 8 * (c + CPR / 2), *(const u32x4*)ob);
+  } else {
+    float v[8];
+    unpack8<T>(ld16(src + 8 * c), v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rope_rotate(v[2 * q], v[2 * q + 1], pos, rh[4 * c + q], rl[4 * c + q]);
+    T o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = Elem<T>::from_float(v[e]);
+    st16(dst + 8 * c, *(const u32x4*)o);
+  }
+}
+
+template <typename T>
+hipError_t rope_t(const void* x, void* y, int64_t BH, int N, int D, int pos_base,
+                  const RopeArgs& rope, hipStream_t st) {
+  const int64_t nrows = BH * N;
+  const int per_row = rope.style == 0 ? D / 16 : D / 8;
+  const int64_t grid = (nrows * per_row + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (D == 64)
+    hipLaunchKernelGGL((rope_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x,
+                       (T*)y, nrows, N, pos_base, rope);
+  else
+    hipLaunchKernelGGL((rope_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)x,
+                       (T*)y, nrows, N, pos_base, rope);
   return hipGetLastError();
 }
 
@@ -510,9 +616,19 @@ hipError_t prefill_quant_t(const FwdArgs& a, const int8_t* qc, const float* qs, 
 }  // namespace
 
 hipError_t launch_quant_int8(const void* x, int elem, int64_t BH, int N, int D, int8_t* codes,
-                             float* scales, hipStream_t s) {
-  return elem == 2 ? quant_int8_t<__bf16>(x, BH, N, D, codes, scales, s)
-                   : quant_int8_t<_Float16>(x, BH, N, D, codes, scales, s);
+                             float* scales, hipStream_t s, const RopeArgs* rope, int pos_base) {
+  RopeArgs none;
+  none.on = 0;
+  none.style = 0;
+  const RopeArgs& r = rope ? *rope : none;
+  return elem == 2 ? quant_int8_t<__bf16>(x, BH, N, D, codes, scales, s, r, pos_base)
+                   : quant_int8_t<_Float16>(x, BH, N, D, codes, scales, s, r, pos_base);
+}
+
+hipError_t launch_rope(const void* x, void* y, int elem, int64_t BH, int N, int D, int pos_base,
+                       const RopeArgs& rope, hipStream_t s) {
+  return elem == 2 ? rope_t<__bf16>(x, y, BH, N, D, pos_base, rope, s)
+                   : rope_t<_Float16>(x, y, BH, N, D, pos_base, rope, s);
 }
 
 hipError_t launch_quant_e4m3(const void* x, int elem, int64_t BH, int N, int D, uint8_t* codes,

@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
               "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
+              "attn_fwd_rope", "attn_fwd_rope_workspace_bytes",
               "attn_status_string"):
         assert n in names
 
@@ -218,3 +219,29 @@ def test_mx_entry_points_reject_before_enqueue(lib):
     # INT8 codes of Q and K, E4M3 codes of V (1 byte each), V's scale bytes (one
     # per 32 keys of a channel) and the fp32 scales of Q's and K's 64-token blocks
     assert need >= 3 * 40 * 32760 * 128 + 40 * 32760 * 128 // 32 + 2 * 40 * 512 * 4
+
+
+
+@pytest.mark.parametrize("rope,want", [
+    (dict(style=2), E_INVALID),
+    (dict(scaling=3), E_INVALID),
+    (dict(base=0.0), E_INVALID),
+    (dict(base=float("inf")), E_INVALID),
+    (dict(scaling=1, factor=0.5), E_INVALID),
+    (dict(scaling=2, factor=2.0, orig_ctx=0), E_INVALID),
+    (dict(scaling=2, factor=2.0, beta_fast=1.0, beta_slow=1.0), E_INVALID),
+    (dict(), E_WORKSPACE),          # valid: fp32 inputs still need their staging workspace
+])
+def test_rope_rejects_before_enqueue(lib, rope, want):
+    r = sdpa.Rope(**rope)
+    st = lib.attn_fwd_rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 0, 0, 0, 0.125, 0, 0,
+                           ctypes.byref(r), None, 0, None)
+    assert st == want
+
+
+def test_rope_workspace_bytes(lib):
+    ws = lib.attn_fwd_rope_workspace_bytes
+    # exact bf16 prefill: room for the rotated K only
+    assert ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 0, 2) >= 40 * 32760 * 128 * 2
+    assert ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 0, 2) < 2 * 40 * 32760 * 128 * 2
+    assert ws(1, 3, 2, 8, 8, 64, 0, 0, 0, 0, 2) == 0    # rejected shape

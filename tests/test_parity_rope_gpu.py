@@ -1,0 +1,91 @@
+"""GPU parity of rotary position embedding (attn_fwd_rope), called through the
+C ABI, against the fp64 oracle (which turns Q and K in double precision and
+then takes exact attention). The exact mode is held to the exact-mode bar; the
+rotated Q and K are rounded to the operand type once more than in the oracle,
+well inside it. The quantised and MX modes are held to their 6e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_dot_product_amd as sdpa
+from scaled_dot_product_amd.inputs import WORKLOADS, Workload, make_qkv, sample_rows
+
+from _parity import EXACT_ABS, EXACT_REL, QUANT_REL, announce, masked_rows, metrics
+
+pytestmark = pytest.mark.gpu
+
+BF, F16, F32 = torch.bfloat16, torch.float16, torch.float32
+PLAIN = dict(style=0, scaling=0, base=10000.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sdpa.load_library()
+
+
+def _check(w, rope, rows=None):
+    announce(f"rope {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} {w.dtype} "
+             f"causal={w.causal} window_lo={w.window_lo} pos0={w.pos0} mode={w.mode} rope={rope}")
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    r = sdpa.Rope(**rope)
+    out = sdpa.fwd_rope(q.to(dev), k.to(dev), v.to(dev), r, causal=w.causal, window_lo=w.window_lo,
+                        pos0=w.pos0, scale=w.scale, mode=w.mode)
+    torch.cuda.synchronize()
+    out = out.double().cpu()
+    assert torch.isfinite(out).all()
+    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, **rope)
+    if rows is None:
+        ref = oracle.attn_rope(q, k, v, **kw)
+        got = out.numpy()
+    else:
+        ref = oracle.attn_rope(q, k, v, rows=rows, **kw)
+        got = out.reshape(-1, w.D)[torch.from_numpy(rows)].numpy()
+    rel, mabs = metrics(got, ref)
+    print(f"    rel={rel:.3e} max_abs={mabs:.3e}", flush=True)
+    if w.mode == 0:
+        assert rel <= EXACT_REL, rel
+        assert mabs <= EXACT_ABS, mabs
+    else:
+        assert rel <= QUANT_REL, rel
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
+
+
+ROPES = [
+    PLAIN,
+    dict(style=1, scaling=0, base=10000.0),
+    dict(style=0, scaling=1, base=10000.0, factor=8.0),
+    dict(style=1, scaling=2, base=500000.0, factor=4.0, orig_ctx=256, beta_fast=32.0, beta_slow=1.0),
+]
+
+
+@pytest.mark.parametrize("rope", ROPES, ids=["plain", "interleaved", "ntk", "yarn"])
+def test_rope_prefill_bf16(rope):
+    _check(Workload("rope", 1, 4, 2, 300, 300, 128, BF, causal=True), rope)
+
+
+@pytest.mark.parametrize("case", [(64, F16, False, 0, 0), (128, F32, True, 40, 100), (64, BF, True, 0, 900)])
+def test_rope_prefill_shapes(case):
+    D, dt, causal, wlo, pos0 = case
+    _check(Workload("rope_shapes", 2, 2, 1, 200, 260 + pos0 // 4, D, dt, causal=causal, window_lo=wlo,
+                    pos0=pos0 if causal else 0), ROPES[3] if dt == F32 else PLAIN)
+
+
+def test_rope_large_positions_sampled():
+    # positions up to 32 759: the angle reduction must keep its precision
+    w = WORKLOADS["video_dit_bf16_32760"].variant(name="rope_video_4heads", Hq=4, Hkv=4)
+    _check(w, ROPES[0], rows=sample_rows(w, 128))
+
+
+@pytest.mark.parametrize("rope", [ROPES[0], ROPES[3]], ids=["plain", "yarn"])
+def test_rope_decode(rope):
+    _check(WORKLOADS["gqa_decode_f16_4096"], rope)
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["quant", "mx"])
+def test_rope_low_precision_modes(mode):
+    _check(Workload("rope_lp", 1, 2, 2, 600, 600, 128, BF, causal=True, mode=mode), ROPES[2])
