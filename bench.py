@@ -6,7 +6,8 @@ in section 1 of "Attention kernels on a home RTX 5080" times its kernels. The
 same run also measures the other shapes of the hot path: the few-row GQA
 decode (cold K/V, rotated over 48 caches so the 256 MB Infinity Cache cannot
 hold them), the quantised INT8-QK / FP8-PV mode and the MX mode (MX FP8
-blocks on the P V product) on the video shape, the
+blocks on the P V product) and rotary position embedding on the video
+shape, the
 SDXL 1024px shape, the causal video shape with a per-row sliding window of
 4096 keys, and the decode over a quantised (INT8 K / E4M3 V) KV cache. It
 prints ONE JSON line.
@@ -248,6 +249,24 @@ def run_extra(part):
                        "tops": round(wm.flops() / (ms_m * 1e-3) / 1e12, 2),
                        "frac_of_fp8_peak": round(wm.flops() / (ms_m * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
         log(f"mx: {ms_m:.3f} ms/call incl. preparation")
+    elif part == "rope":
+        import torch
+        import scaled_dot_product_amd as sdpa
+        wr = WORKLOADS["video_dit_bf16_32760"]
+        dev = torch.device("cuda:0")
+        q, k, v = (t.to(dev) for t in inputs(wr))
+        out = torch.empty_like(q)
+        rope = sdpa.Rope(style=sdpa.ROPE_HALF, scaling=sdpa.ROPE_PLAIN, base=10000.0)
+        ws = torch.empty(max(sdpa.fwd_rope_workspace_bytes(wr.B, wr.Hq, wr.Hkv, wr.Nq, wr.Nk, wr.D,
+                                                            dtype=wr.dtype), 1),
+                         dtype=torch.uint8, device=dev)
+        ms_r = time_events(lambda: sdpa.fwd_rope(q, k, v, rope, scale=wr.scale, out=out,
+                                                 workspace=ws), 10, 2)
+        extra["rope"] = {"workload": "video_dit_rope_bf16_32760", "ms_per_call": round(ms_r, 4),
+                         "tflops": round(wr.flops() / (ms_r * 1e-3) / 1e12, 2),
+                         "frac_of_bf16_peak": round(wr.flops() / (ms_r * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"rope: {ms_r:.3f} ms/call (K turned in one pass, Q in the kernel)")
+        del q, k, v, out, ws
     elif part == "causal":
         wc = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_causal_bf16_32760", causal=True)
         ms_c = bench_prefill(wc, 10, 2)
@@ -367,8 +386,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "mx", "causal", "sliding",
-                                       "sdxl", "copy"],
+    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "mx", "rope", "causal",
+                                       "sliding", "sdxl", "copy"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -402,7 +421,7 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "mx", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
+        for part in ("quant", "mx", "rope", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
             extra.update(run_extra(part))
 
     cpu = None if args.skip_cpu else cpu_baseline(w)
