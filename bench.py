@@ -394,8 +394,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each GPU would run independent heads, or key ranges merged by log-sum-exp).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -39,7 +39,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_E_INVALID = -1,     /* null/misaligned pointer, bad size, bad scale  */
-  ATTN_E_UNSUPPORTED = -2, /* head dim, dtype or mode this build lacks      */
+  ATTN_E_UNSUPPORTED = -2, /* head dim, dtype, mode or shape not supported  */
   ATTN_E_WORKSPACE = -3,   /* workspace smaller than attn_fwd_workspace_bytes */
   ATTN_E_HIP = -4          /* the HIP runtime refused a launch              */
 } attn_status;
