@@ -40,7 +40,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_E_INVALID = -1,     /* null/misaligned pointer, bad size, bad scale  */
   ATTN_E_UNSUPPORTED = -2, /* head dim, dtype, mode or shape not supported  */
-  ATTN_E_WORKSPACE = -3,   /* workspace smaller than attn_fwd_workspace_bytes */
+  ATTN_E_WORKSPACE = -3,   /* workspace below the matching *_workspace_bytes */
   ATTN_E_HIP = -4          /* the HIP runtime refused a launch              */
 } attn_status;
 
@@ -57,15 +57,14 @@ typedef enum {
                           scales ("SageAttention 2 INT8 QK . FP8 PV" row of
                           the table in section 1 of "Attention kernels on a
                           home RTX 5080"); bf16/f16 inputs only */
-  ATTN_MODE_MX = 2     /* OCP MX FP8 blocks everywhere: Q and K in blocks of
-                          32 channels, V in blocks of 32 keys (attn_quantize_mx),
-                          the softmax weights in blocks of 32 keys of each row;
-                          both products on the scaled FP8 matrix cores with
-                          the E8M0 block scales as operands (the per-block-
-                          scaled low-precision kernels of that table, MXFP as
-                          in "Transformers Get a Turbo Boost with
-                          Mixed-Precision Magic"); bf16/f16 inputs only; head
-                          dim 64 or 128 */
+  ATTN_MODE_MX = 2     /* INT8 Q K^T as in ATTN_MODE_QUANT, and P V in OCP
+                          MX FP8 blocks: V in blocks of 32 keys of each
+                          channel (attn_quantize_mx, axis 1), the softmax
+                          weights in blocks of 32 keys of each row, both E8M0
+                          block scales applied by the scaled FP8 matrix cores
+                          (the per-block-scaled low-precision kernels of that
+                          table, MXFP as in "Transformers Get a Turbo Boost
+                          with Mixed-Precision Magic"); bf16/f16 inputs only */
 } attn_mode;
 
 /*
