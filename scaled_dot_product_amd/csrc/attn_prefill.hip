@@ -17,8 +17,10 @@
 //
 // The loop is software-pipelined so that both halves of the work always have
 // matrix-core instructions beside them: iteration i first accumulates P V of
-// tile i-1 on the MFMA pipe while the vector ALU takes the row maxima of tile
-// i, then computes S of tile i+1 while the vector ALU exponentiates tile i.
+// tile i-1 on the MFMA pipe while the vector ALU exponentiates half of tile
+// i, then computes S of tile i+1 beside the other half. The weights are
+// taken against the running maximum as it stands; the tile's row maxima are
+// computed only in the rare branch that raises it.
 // K tiles are loaded two iterations ahead, V tiles one; K and V use separate
 // LDS double buffers and one barrier per iteration suffices. The instruction
 // interleave inside each half is fixed with scheduling-group barriers.
@@ -35,11 +37,11 @@ namespace attn {
 
 namespace {
 
-// The running maximum is raised only when a new score exceeds it by more
-// than this many powers of two; until then exponents stay <= 2^8, which bf16,
-// f16 and fp32 hold exactly in range. Exactness is unaffected: numerator and
-// denominator share the stale maximum.
-constexpr float kLazyLog2 = 8.0f;
+// The running maximum is raised only when some weight against it could
+// exceed this bound (a lane's partial row sum of a tile does); until then the
+// weights stay <= 2^12, which bf16, f16 and fp32 hold in range. Exactness is
+// unaffected: numerator and denominator share the stale maximum.
+constexpr float kLazyMax = 4096.0f;
 
 // Scheduling-group masks (see the AMDGPU backend's sched_group_barrier).
 constexpr int kSchedValu = 0x002;
@@ -252,9 +254,8 @@ prefill_kernel(FwdArgs a, int ntq) {
         }
   };
 
-  // One pipeline step for tile i (scores in cur): P V of tile i - 1 beside
-  // the row maxima of tile i, then S of tile i + 1 into nxt beside the
-  // exponentials of tile i.
+  // One pipeline step for tile i (scores in cur): P V of tile i - 1, then S
+  // of tile i + 1 into nxt, each beside half of the exponentials of tile i.
   auto step = [&](auto first, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     constexpr bool kFirst = decltype(first)::value;
     const int t = t_lo + i;
@@ -276,19 +277,20 @@ prefill_kernel(FwdArgs a, int ntq) {
           p[tt][q] = E::from_float(__builtin_amdgcn_exp2f(fmaf(cur[mb][8 * tt + q], a.c, -mu_)));
     };
 
-    // First half: P V of tile i - 1 on the MFMA pipe beside the row maxima of
-    // tile i and, speculatively against the current running maximum, the
-    // weights of its first 32 keys (redone in the rare rescale branch), so
-    // that both halves carry about the same vector work.
+    // The weights of tile i are taken against the running maximum as it
+    // stands; the row maxima of the tile are needed only when a weight may
+    // exceed kLazyMax or the row has no maximum yet. A lane's partial row sum
+    // bounds each of its weights, so the sums the denominator needs anyway
+    // decide that, and the maxima are found in the rare rescale branch.
+    // First half: P V of tile i - 1 on the MFMA pipe beside the weights of
+    // the first 32 keys; second half: S of tile i + 1 beside the other 32.
     if constexpr (!kFirst) pv_mma((i - 1) & 1);
-    float mx = cur[0][0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, cur[0][j]);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][j]);
-    mx = halves_max(mx) * a.c;
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
     V8 pa[2], pb[2];
-    weights(0, m_run == -INFINITY ? 0.0f : m_run, pa);
+    weights(0, mu, pa);
+    float ls[4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) ls[tt] = E::sum8(pa[tt], 0.0f);
     if constexpr (!kFirst) {
       // 4 DB MFMAs with the vector work spread between them; transpose reads
       // run ahead of the MFMAs that use them.
@@ -296,24 +298,46 @@ prefill_kernel(FwdArgs a, int ntq) {
 #pragma unroll
       for (int k = 0; k < 4 * DB; ++k) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (4 * DB), 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 48 / (4 * DB), 0);
         if (k < 4 * DB - kVPre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
     {
-      // keep the speculative weights in this half (the compiler would sink
-      // them past the branch below)
+      // keep the first weights in this half (the compiler would sink them
+      // into the second)
       u32x4 w0 = __builtin_bit_cast(u32x4, pa[0]);
       u32x4 w1 = __builtin_bit_cast(u32x4, pa[1]);
-      asm volatile("" : "+v"(w0), "+v"(w1));
+      asm volatile("" : "+v"(w0), "+v"(w1), "+v"(ls[0]), "+v"(ls[1]));
       pa[0] = __builtin_bit_cast(V8, w0);
       pa[1] = __builtin_bit_cast(V8, w1);
     }
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
-      // rare after the first tiles; the empty asm keeps this a real branch
-      // (the compiler would otherwise run the rescale on every tile). O
-      // already holds tile i - 1 here.
+
+    s_mma((i + 1) & 1, nxt);
+    weights(1, mu, pb);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) ls[2 + tt] = E::sum8(pb[tt], 0.0f);
+    // 2*KS MFMAs with the vector work spread between them; the K reads run
+    // ahead of the MFMAs that use them.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKPre, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * KS - kKPre; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 48 / (2 * KS), 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKPre, 0);
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // (!(x <= y) also catches a NaN partial sum)
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kLazyMax) || m_run == -INFINITY)) {
+      // rare after a row's first tile; the empty asm keeps this a real branch.
+      // O already holds tile i - 1 here.
       asm volatile("" ::: "memory");
+      float mx = cur[0][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, cur[0][j]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[1][j]);
+      mx = halves_max(mx) * a.c;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -322,32 +346,14 @@ prefill_kernel(FwdArgs a, int ntq) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
       m_run = m_new;
-      weights(0, m_run == -INFINITY ? 0.0f : m_run, pa);
-    }
-    const float mu = m_run == -INFINITY ? 0.0f : m_run;
-
-    // Second half: S of tile i + 1 (MFMA) beside the weights of the other 32
-    // keys of tile i and the row sums.
-    s_mma((i + 1) & 1, nxt);
-    weights(1, mu, pb);
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    // the denominator sums the rounded weights the P V product uses
+      const float mu2 = m_run == -INFINITY ? 0.0f : m_run;
+      weights(0, mu2, pa);
+      weights(1, mu2, pb);
+      lsum = 0.0f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      ls[tt] = E::sum8(pa[tt], ls[tt]);
-      ls[2 + tt] = E::sum8(pb[tt], ls[2 + tt]);
+      for (int tt = 0; tt < 2; ++tt) lsum = E::sum8(pb[tt], E::sum8(pa[tt], lsum));
     }
-    // 2*KS MFMAs with the vector work spread between them; the K reads run
-    // ahead of the MFMAs that use them.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKPre, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * KS - kKPre; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (2 * KS), 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKPre, 0);
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    l_run += lsum;
     // Pin the weights here: left alone, the compiler sinks the exponentials
     // past the barrier to their first use in the next step, where the P V
     // MFMAs would wait on them and no MFMA would run beside them.
