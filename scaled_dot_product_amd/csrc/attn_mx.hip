@@ -261,7 +261,14 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
     for (int u = 0; u < NV; ++u) load_to_lds16(base, vofs[u], &sv[buf][((D / 4) * wave + 16 * u) * 64]);
     // the tile's 2 D scale bytes ride along (wave 1)
-    if (wave == 1 && lane < NVS) load_to_lds16(Vs + (int64_t)t * 2 * D, (uint32_t)(16 * lane), &svs[buf][0]);
+    // (the byte offset is rebuilt from the lane id on the spot: kept across
+    // the loop, it is spilled at head dim 128)
+    if (wave == 1 && lane < NVS) {
+      uint32_t ofs;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0"
+                   : "=v"(ofs));
+      load_to_lds16(Vs + (int64_t)t * 2 * D, ofs, &svs[buf][0]);
+    }
   };
 
   f32x16 oacc[DB];
@@ -288,6 +295,13 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       }
   };
 
+  // E4M3 1.0 in every byte, and a zero accumulator
+  i32x8 ones8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones8[j] = 0x38383838;
+  f32x16 fzero;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) fzero[j] = 0.0f;
   auto step = [&](int i, i32x16 (&cur)[2], i32x16 (&nxt)[2]) {
     const int t = t_lo + i;
     if (i + 2 < nt) load_k(t + 2, i & 1);
@@ -361,7 +375,6 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 
     // S of tile i + 1 beside the weights of tile i.
     s_mma((i + 1) & 1, nxt);
-    float ls[2] = {0.0f, 0.0f};
     i32x8 pb;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -369,17 +382,20 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       for (int q4 = 0; q4 < 4; ++q4) {
         float e[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -Cm[mb]));
-          ls[mb] += e[k];
-        }
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        for (int k = 0; k < 4; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -Cm[mb]));
+        // (the second conversion writes the upper half, so the first one may
+        // start from whatever the register holds: no zeroing move)
+        int pk;
+        asm volatile("" : "=v"(pk));
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk, false);
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
         pb[4 * mb + q4] = pk;
       }
-    // the denominator takes the weights back to their unscaled values
-    l_run += __builtin_amdgcn_ldexpf(ls[0], E[0]) + __builtin_amdgcn_ldexpf(ls[1], E[1]);
     const int psc = (half ? E[1] : E[0]) + 127;   // lane half h: scale of block h
+    // The denominator: the tile's row sums of the weights the numerator uses,
+    // in unscaled units, from one more scaled MFMA against an all-ones block
+    // (every row of the product is the same column sum).
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pb, fzero, 0, 0, 0, 127, 0, psc);
 
     // O^T += V^T P^T for tile i: one scaled FP8 MFMA per 32 channels (a
     // scheduling fence keeps the V operand reads from being hoisted above
@@ -397,6 +413,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       const int vsc = svs[vb][half * D + d];
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, vsc, 0, psc);
     }
+    l_run += rs[0];
     vmem_wait_all();
     __syncthreads();
   };
@@ -418,7 +435,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     if (i < nt) step(i, s0, s1);
   }
 
-  const float l = halves_sum(l_run);
+  const float l = l_run;   // both lane halves hold the row's full sum
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (qrow < a.Nq) {
     TO* orow = Op + (int64_t)qrow * D;

@@ -19,7 +19,8 @@
 //                                     the largest one the query tile sees;
 //                                     folded into the exponent's bias)
 //     O_acc += Vc^T P^T              fp8 MFMA 32x32x64, fp32 accumulation
-//     l += sum of P (unquantised)
+//     l += (row sums of P^) * s_ref / (112 s_v)   (the sums from one more fp8
+//                                     MFMA against an all-ones block)
 //   O = O_acc * s_ref / 112 / l.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
@@ -215,8 +216,8 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
 // E4M3(112 P s_v / s_ref) with s_ref the largest V block scale the query tile
 // sees: the factor 112 s_v / s_ref <= 112 goes into the exponent's bias
 // (free), the fp8 products accumulate straight into O, and the epilogue
-// multiplies by s_ref / 112 once. The denominator sums the unquantised
-// weights (the exponentials taken back by the same per-tile factor).
+// multiplies by s_ref / 112 once. The denominator sums the quantised
+// weights the numerator uses, taken back by the same per-tile factor.
 template <typename TO, int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
@@ -273,6 +274,9 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
   if (lane == 0) sred[wave] = sref;
   __syncthreads();
   sref = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+  // (the tile factor s_v / s_ref scales a tile's numerator and denominator
+  // alike, so a reciprocal's rounding cancels)
+  const float inv_sref = sref > 0.0f ? 1.0f / sref : 0.0f;
 
   const int qrow = q0 + wave * 32 + col;
   const int qw0 = q0 + wave * 32;
@@ -366,6 +370,14 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
       }
   };
 
+  // E4M3 1.0 in every byte, and a zero accumulator
+  i32x8 ones8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones8[j] = 0x38383838;
+  asm volatile("" : "+v"(ones8));   // kept in registers, not rebuilt per tile
+  f32x16 fzero;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) fzero[j] = 0.0f;
   auto step = [&](int i, i32x16 (&cur)[2], i32x16 (&nxt)[2]) {
     const int t = t_lo + i;
     if (i + 2 < nt) load_k(t + 2, i & 1);
@@ -375,7 +387,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     // of such a block is exactly 0.
     const float cf = fmaxf(cq * Ks[t], 1.17549435e-38f);
     const float sv_t = Vs[t];
-    const float ratio = sref > 0.0f ? fmaxf(sv_t / sref, 9.5367431640625e-7f) : 1.0f;
+    const float ratio = sref > 0.0f ? fmaxf(sv_t * inv_sref, 9.5367431640625e-7f) : 1.0f;
     const float bias = __builtin_amdgcn_logf(ratio) + (kLog2_448 - kMargin - kLag);   // log2
     constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
     float sf[2][16];                      // kOff + S
@@ -435,18 +447,18 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     // S of tile i + 1 (i8 MFMA) interleaved with the weights of tile i.
     s_mma((i + 1) & 1, nxt);
     i32x8 pb;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         float e[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -C));
-          ls[k] += e[k];
-        }
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        for (int k = 0; k < 4; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -C));
+        // (the second conversion writes the upper half, so the first one may
+        // start from whatever the register holds: no zeroing move)
+        int pk;
+        asm volatile("" : "=v"(pk));
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk, false);
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
         pb[4 * mb + q4] = pk;
       }
@@ -454,12 +466,14 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
 #pragma unroll
     for (int k = 0; k < 2 * KS - 2; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * KS), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 80 / (2 * KS), 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    // back to unscaled weights for the denominator
-    l_run += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * __builtin_amdgcn_exp2f(-bias);
+    // The tile's row sums of the FP8 weights, from one more MFMA against an
+    // all-ones block (every row of the product is the same column sum), taken
+    // back to unscaled weights for the denominator.
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pb, fzero, 0, 0, 0, 127, 0, 127);
 
     // O^T += V^T P^T (fp8 x fp8 -> fp32) for tile i: one MFMA per 32 channels.
     const int vb = i & 1;
@@ -473,6 +487,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, 127, 0, 127);
     }
+    l_run += rs[0] * __builtin_amdgcn_exp2f(-bias);
     vmem_wait_all();
     __syncthreads();
   };
@@ -494,7 +509,7 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
     if (i < nt) step(i, s0, s1);
   }
 
-  const float l = halves_sum(l_run);
+  const float l = l_run;   // both lane halves hold the row's full sum
   // undo the fp8 weight scaling: 448 * 2^-(margin + lag) / s_ref
   const float inv = l > 0.0f ? (sref * __builtin_amdgcn_exp2f(kMargin + kLag) / 448.0f) / l : 0.0f;
   if (qrow < a.Nq) {

@@ -239,9 +239,10 @@ def test_quant_mode_small(case):
 
 def test_quant_mode_zero_q_closed_form():
     # Q = 0: every score is 0 and every weight 1. Key block t's weights are
-    # rounded once, to E4M3(448 s_v,t / s_ref) / (448 s_v,t / s_ref) with s_ref
-    # the largest V block scale the query tile sees, so the output is the
-    # block-weighted mean of V^ with those factors (plain mean where s_v,t = s_ref).
+    # rounded once, to E4M3(448 s_v,t / s_ref) / (448 s_v,t / s_ref) = w_t with
+    # s_ref the largest V block scale the query tile sees; numerator and
+    # denominator both use the rounded weights, so the output is the w_t-weighted
+    # mean of V^ over the keys (plain mean where s_v,t = s_ref).
     w = Workload("qzero", 1, 2, 2, 64, 300, 128, torch.bfloat16, mode=1)
     _, k, v = make_qkv(w)
     q = torch.zeros(w.q_shape, dtype=torch.bfloat16)
@@ -255,7 +256,8 @@ def test_quant_mode_zero_q_closed_form():
         ratio = s_v / s_v.max()
         wt = np.array([oracle.e4m3_decode(oracle.e4m3_encode(np.float32(448.0 * r))) / (448.0 * r)
                        for r in ratio])
-        want = (np.repeat(wt, 64)[:300, None] * vhat).sum(axis=0) / 300.0
+        wk = np.repeat(wt, 64)[:300, None]
+        want = (wk * vhat).sum(axis=0) / wk.sum()
         np.testing.assert_allclose(out[0, h], np.broadcast_to(want, (64, 128)), rtol=0, atol=1e-3)
         gap = max(gap, np.abs(want - vhat.mean(axis=0)).max())
     # the per-block factors are not all 1 here, so this also checks they are applied
