@@ -194,6 +194,33 @@ def decode_bytes(w):
     return kv + 2 * w.B * w.Hq * w.Nq * w.D * 2
 
 
+# Ops per MFMA of the rate probe's kinds: bf16 32x32x16, int8 32x32x32, fp8 32x32x64.
+PROBE_OPS = {0: 32768.0, 1: 65536.0, 2: 131072.0}
+
+
+def measured_peaks():
+    """What this part sustains on the box: the MFMA rate probe (register
+    operands, 2 waves per SIMD, no memory traffic) per dtype, and a 1 GiB device
+    copy for HBM (bytes read + written)."""
+    import torch
+    import scaled_dot_product_amd as sdpa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 512
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    res = {}
+    for kind, key in ((0, "bf16_tflops"), (1, "int8_tops"), (2, "fp8_tops")):
+        ms = time_events(lambda: sdpa.probe_mfma(kind, iters, blocks, out), 5, 2)
+        res[key] = round(blocks * 4 * iters * 16 * PROBE_OPS[kind] / (ms * 1e-3) / 1e12, 1)
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    ms = time_events(lambda: y.copy_(x), 5, 2)
+    res["copy_gbs"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    log(f"measured peaks: {res}")
+    return res
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on a bounded sample of rows of w (host cores)."""
     import numpy as np
@@ -425,6 +452,18 @@ def main():
         for part in ("quant", "mx", "rope", "causal", "sliding", "sdxl", "decode", "decode_kvq"):
             extra.update(run_extra(part))
 
+    peaks = measured_peaks()
+    if "quant" in extra:
+        extra["quant"]["frac_of_measured_int8_fp8"] = round(
+            extra["quant"]["tops"] / (0.5 * (peaks["int8_tops"] + peaks["fp8_tops"])), 4)
+    if "mx" in extra:
+        extra["mx"]["frac_of_measured_int8_fp8"] = round(
+            extra["mx"]["tops"] / (0.5 * (peaks["int8_tops"] + peaks["fp8_tops"])), 4)
+    for key in ("decode", "decode_kvq"):
+        if key in extra:
+            extra[key]["frac_of_measured_copy_cold"] = round(extra[key]["gbs_cold"] / peaks["copy_gbs"], 4)
+    extra["measured_peaks"] = peaks
+
     cpu = None if args.skip_cpu else cpu_baseline(w)
     if cpu:
         log(f"cpu baseline: {cpu['value']} TFLOP/s on {cpu['cores']} threads")
@@ -449,6 +488,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_video_dit_traffic.json"),
                      "kernel": "prefill_kernel<bf16,bf16,128>",
+                     "measured_peak": peaks["bf16_tflops"],
+                     "frac_of_measured": round(tflops / peaks["bf16_tflops"], 4),
                      "per_launch": "21.979 TFLOP (4*B*H*N*N*D)"},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -284,6 +284,20 @@ size_t attn_decode_kvq_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, i
 /* Static English text for a status code. */
 const char* attn_status_string(int status);
 
+/* Measurement helper, not part of attention: a matrix-core rate probe.
+ * Launches `blocks` workgroups of 256 threads (4 waves); every wave issues
+ * iters * 16 MFMAs with register operands on four independent accumulators:
+ *   kind 0: bf16 v_mfma_f32_32x32x16_bf16       (32 768 flop each)
+ *   kind 1: int8 v_mfma_i32_32x32x32_i8         (65 536 op each)
+ *   kind 2: fp8  v_mfma_scale_f32_32x32x64_f8f6f4, unit scales (131 072 op each)
+ * so ops per launch = blocks * 4 * iters * 16 * (ops per MFMA), and that over
+ * the launch's time is the rate this part sustains for that MFMA alone.
+ * out: caller-owned device memory for blocks * 256 floats (one sum per thread,
+ * which keeps the work live). Asynchronous on `stream`.
+ * Errors: ATTN_E_INVALID for a null or misaligned out, kind outside 0..2,
+ * iters < 1, or blocks outside 1..65535; ATTN_E_HIP for a launch failure. */
+int attn_probe_mfma(int kind, int iters, int blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_b
            "fwd_rope", "fwd_rope_workspace_bytes", "Rope", "ROPE_HALF", "ROPE_INTERLEAVED",
            "ROPE_PLAIN", "ROPE_NTK", "ROPE_YARN",
            "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
-           "decode_kvq_workspace_bytes", "load_library",
+           "decode_kvq_workspace_bytes", "probe_mfma", "load_library",
            "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -84,6 +84,8 @@ def load_library():
     lib.attn_decode_kvq_workspace_bytes.restype = sz
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_probe_mfma.argtypes = [i, i, i, vp, vp]
+    lib.attn_probe_mfma.restype = i
     _lib = lib
     return lib
 
@@ -311,3 +313,15 @@ def decode_kvq(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
                              int(pos0), float(scale), dt, ws_ptr, ws_len, _stream_handle(q))
     _check(st, "attn_decode_kvq")
     return out
+
+
+def probe_mfma(kind: int, iters: int, blocks: int, out: torch.Tensor) -> None:
+    """Matrix-core rate probe on the current stream (measurement only): blocks
+    workgroups of 4 waves, each wave iters * 16 MFMAs of the given kind (0 bf16
+    32x32x16, 1 int8 32x32x32, 2 fp8 32x32x64); out: float32 device tensor of
+    blocks * 256 elements."""
+    lib = load_library()
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * 256:
+        raise AttnError("probe_mfma: out must be a float32 device tensor of blocks * 256 elements")
+    _check(lib.attn_probe_mfma(int(kind), int(iters), int(blocks), ctypes.c_void_p(out.data_ptr()),
+                               _stream_handle(out)), "attn_probe_mfma")

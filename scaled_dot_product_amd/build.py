@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_prefill.hip", "attn_decode.hip", "attn_quant.hip", "attn_mx.hip"]
+SOURCES = ["attn_api.cpp", "attn_prefill.hip", "attn_decode.hip", "attn_quant.hip", "attn_mx.hip",
+           "attn_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

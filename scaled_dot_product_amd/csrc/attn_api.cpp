@@ -407,6 +407,15 @@ int attn_decode_kvq(const void* q, const int8_t* k_codes, const float* k_scales,
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+int attn_probe_mfma(int kind, int iters, int blocks, float* out, void* stream) {
+  if (out == nullptr || !aligned16(out) || kind < 0 || kind > 2 || iters < 1 || blocks < 1 ||
+      blocks > 65535)
+    return ATTN_E_INVALID;
+  return attn::launch_probe_mfma(kind, iters, blocks, out, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK
+             : ATTN_E_HIP;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -98,4 +98,7 @@ hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs
                              const int8_t* kc, const float* ks, const uint8_t* vct,
                              const uint8_t* vs, int elem_out, hipStream_t s);
 
+// Matrix-core rate probe (attn_probe.hip).
+hipError_t launch_probe_mfma(int kind, int iters, int blocks, float* out, hipStream_t s);
+
 }  // namespace attn

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
               "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
               "attn_fwd_rope", "attn_fwd_rope_workspace_bytes",
-              "attn_status_string"):
+              "attn_status_string", "attn_probe_mfma"):
         assert n in names
 
 
@@ -202,6 +202,16 @@ def test_sliding_workspace_bytes(lib):
     assert ws(1, 16, 8, 4, 4096, 128, 1, 1000, 4092, 0, 1) > 0          # decode partials
     assert ws(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0, 1) == 0            # window 0 rejected
 
+
+
+def test_probe_rejects_before_enqueue(lib):
+    p = lib.attn_probe_mfma
+    assert p(0, 4, 2, None, None) == E_INVALID          # no output buffer
+    assert p(0, 4, 2, FAKE + 4, None) == E_INVALID      # misaligned
+    assert p(3, 4, 2, FAKE, None) == E_INVALID          # unknown kind
+    assert p(0, 0, 2, FAKE, None) == E_INVALID          # no iterations
+    assert p(1, 4, 0, FAKE, None) == E_INVALID          # no workgroups
+    assert p(2, 4, 65536, FAKE, None) == E_INVALID      # grid too large
 
 
 def test_mx_entry_points_reject_before_enqueue(lib):
