@@ -111,9 +111,9 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                 int mode, int dtype);
 
 /*
- * Rotary position embedding (RoPE) of Q and K, the "RoPE with NTK / YaRN
- * scaling inside the kernel" of section "Plans" of "Attention kernels on a
- * home RTX 5080" (the page gives no formulas; the published ones are used).
+ * Rotary position embedding (RoPE) of Q and K inside the kernel, with NTK or
+ * YaRN scaling, as section "Plans" of "Attention kernels on a home RTX 5080"
+ * proposes (the page gives no formulas; the published ones are used).
  * Query row i sits at position pos0 + i, key j at position j. Pair i of a row
  * (i = 0 .. D/2 - 1) turns by the angle position * theta_i:
  *   (a, b) -> (a cos - b sin, a sin + b cos).

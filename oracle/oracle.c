@@ -44,8 +44,8 @@
  * key is visible iff j >= window_lo and (not causal or j <= pos0 + i) and,
  * with a per-row window of width W, j >= pos0 + i - W + 1; the KV
  * head of query head h is h / (Hq / Hkv); a row with no visible key is all
- * zeros ("zeroed inactive regions", section "measured results" of "round 21
- * track b — qsa2"); quantisation blocks are 64 consecutive tokens of one
+ * zeros (the measured-results section of "round 21 track b — qsa2" zeroes
+ * rows outside the active region); quantisation blocks are 64 consecutive tokens of one
  * head, the last block holding the remainder.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
@@ -539,9 +539,9 @@ int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
 /* ------------------------------------------------------------------ RoPE -- */
 
 /*
- * Rotary position embedding, the "RoPE with NTK / YaRN scaling inside the
- * kernel" of section "Plans" of "Attention kernels on a home RTX 5080". The
- * page gives no formulas; the published definitions are followed.
+ * Rotary position embedding with NTK or YaRN scaling, which section "Plans"
+ * of "Attention kernels on a home RTX 5080" proposes to apply inside the
+ * kernel. The page gives no formulas; the published definitions are followed.
  *   plain  theta_i = base^(-2 i / D), i = 0 .. D/2 - 1 (RoFormer);
  *   NTK    the same with base * s^(D / (D - 2)) (NTK-aware scaling, factor s);
  *   YaRN   theta_i' = (1 - g_i) theta_i / s + g_i theta_i, with

@@ -2,8 +2,8 @@
 
 This module draws random numbers and casts them to the element type a workload
 names; it holds none of the attention arithmetic. Q, K and V are i.i.d.
-standard normal (the "random data" on which the table in section 1 of
-"Attention kernels on a home RTX 5080" measures error), drawn in float32 with
+standard normal (random inputs, as the table in section 1 of
+"Attention kernels on a home RTX 5080" uses to measure error), drawn in float32 with
 numpy's PCG64 generator from seeds 41, 42 and 43 (41 is the seed of the parity
 cases in section "build and reproduction" of "round 21 track b — qsa2"), then
 rounded to nearest-even into the workload's dtype.
