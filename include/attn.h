@@ -281,22 +281,75 @@ int attn_decode_kvq(const void* q, const int8_t* k_codes, const float* k_scales,
 size_t attn_decode_kvq_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                        int causal, int window_lo, int pos0, int dtype);
 
+/*
+ * attn_fwd_decode — the split-KV decode of attn_fwd with a caller-chosen
+ * split count (serving loops tune it to the batch and the cache length; the
+ * tests use it to check that the result does not depend on it).
+ *
+ * The G * Nq query rows of a key/value head (G = Hq / Hkv) are packed into one
+ * matrix-core block; the visible keys are cut into 64-key tiles, `splits`
+ * workgroups share a key/value head's tiles (contiguous ranges), each keeps
+ * an online-softmax partial (running max, running sum, unnormalised O), and
+ * the last workgroup of the head to finish merges the partials with
+ * log-sum-exp weights in split order: the chunked attention + merge structure
+ * of "round 21 track b — qsa2" (sections "implementation and review",
+ * "measured results").
+ *
+ *   splits     workgroups per key/value head: 0 = the library's own plan
+ *              (what attn_fwd uses); otherwise at most this many, fewer when
+ *              the visible range has fewer 64-key tiles (at most 64).
+ *   Every other argument, layout and error is as for attn_fwd in the exact
+ *   mode (mode is implied). (Hq / Hkv) * Nq must be <= 32 and B * Hkv <=
+ *   65535, else ATTN_E_UNSUPPORTED; splits < 0 gives ATTN_E_INVALID.
+ *   workspace  at least attn_fwd_decode_workspace_bytes(...) bytes.
+ * Unlike attn_fwd, the decode kernel runs for any number of visible keys
+ * (attn_fwd takes it only for >= 512). Rows with no visible key are zeros.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                    int causal, int window_lo, int pos0, float scale, int dtype, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace attn_fwd_decode needs (host-only; 0 for arguments it rejects). */
+size_t attn_fwd_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                       int causal, int window_lo, int pos0, int dtype,
+                                       int splits);
+
+/*
+ * attn_fwd_plan — which kernels a call would launch, without launching
+ * anything (host-only; the dispatch stays inside the library, as the
+ * resolver of "perf(metal): widen four-row flash KV tiles" keeps it, and this
+ * makes it observable).
+ *
+ * Arguments as for attn_fwd (window > 0 describes attn_fwd_sliding with that
+ * width, window_lo must then be 0; rope nonzero describes attn_fwd_rope).
+ * Fills *plan and returns ATTN_OK, or the status attn_fwd would return for
+ * these sizes (plan untouched).
+ */
+typedef enum {
+  ATTN_KERNEL_PREFILL = 1,        /* exact-mode prefill (bf16/f16 matrix cores) */
+  ATTN_KERNEL_DECODE = 2,         /* exact-mode split-KV decode, fused merge */
+  ATTN_KERNEL_PREFILL_QUANT = 3,  /* INT8 Q K^T, FP8 P V */
+  ATTN_KERNEL_PREFILL_MX = 4      /* INT8 Q K^T, MX FP8 P V */
+} attn_kernel;
+
+typedef struct {
+  int kernel;              /* attn_kernel of the attention launch */
+  int waves;               /* waves of 64 lanes per workgroup */
+  int rows;                /* prefill: query rows per workgroup; decode: packed
+                              query rows per key/value head (G * Nq) */
+  int splits;              /* decode: workgroups per key/value head; else 1 */
+  long long workgroups;    /* workgroups of the attention launch */
+  int pre_launches;        /* launches enqueued before it (fp32 -> bf16
+                              conversions, quantisers, the K rotation pass) */
+  size_t workspace_bytes;  /* what the matching *_workspace_bytes returns */
+} attn_plan;
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int window_lo,
+                  int window, int pos0, int mode, int dtype, int rope, attn_plan* plan);
+
 /* Static English text for a status code. */
 const char* attn_status_string(int status);
-
-/* Measurement helper, not part of attention: a matrix-core rate probe.
- * Launches `blocks` workgroups of 256 threads (4 waves); every wave issues
- * iters * 16 MFMAs with register operands on four independent accumulators:
- *   kind 0: bf16 v_mfma_f32_32x32x16_bf16       (32 768 flop each)
- *   kind 1: int8 v_mfma_i32_32x32x32_i8         (65 536 op each)
- *   kind 2: fp8  v_mfma_scale_f32_32x32x64_f8f6f4, unit scales (131 072 op each)
- * so ops per launch = blocks * 4 * iters * 16 * (ops per MFMA), and that over
- * the launch's time is the rate this part sustains for that MFMA alone.
- * out: caller-owned device memory for blocks * 256 floats (one sum per thread,
- * which keeps the work live). Asynchronous on `stream`.
- * Errors: ATTN_E_INVALID for a null or misaligned out, kind outside 0..2,
- * iters < 1, or blocks outside 1..65535; ATTN_E_HIP for a launch failure. */
-int attn_probe_mfma(int kind, int iters, int blocks, float* out, void* stream);
 
 #ifdef __cplusplus
 }

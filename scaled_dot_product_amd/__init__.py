@@ -9,6 +9,7 @@ fallback: if the library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -19,7 +20,9 @@ __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_b
            "fwd_rope", "fwd_rope_workspace_bytes", "Rope", "ROPE_HALF", "ROPE_INTERLEAVED",
            "ROPE_PLAIN", "ROPE_NTK", "ROPE_YARN",
            "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
-           "decode_kvq_workspace_bytes", "probe_mfma", "load_library",
+           "decode_kvq_workspace_bytes", "fwd_decode", "fwd_decode_workspace_bytes", "plan",
+           "Plan", "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_PREFILL_QUANT", "KERNEL_PREFILL_MX",
+           "load_library", "open_library", "using",
            "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -30,6 +33,7 @@ MODE_MX = 2
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2
+KERNEL_PREFILL, KERNEL_DECODE, KERNEL_PREFILL_QUANT, KERNEL_PREFILL_MX = 1, 2, 3, 4
 
 
 class Rope(ctypes.Structure):
@@ -41,6 +45,13 @@ class Rope(ctypes.Structure):
     def __init__(self, style=ROPE_HALF, scaling=ROPE_PLAIN, base=10000.0, factor=1.0,
                  orig_ctx=4096, beta_fast=32.0, beta_slow=1.0):
         super().__init__(style, scaling, base, factor, orig_ctx, beta_fast, beta_slow)
+
+class Plan(ctypes.Structure):
+    """attn_plan of include/attn.h: the kernels a call would launch."""
+    _fields_ = [("kernel", ctypes.c_int), ("waves", ctypes.c_int), ("rows", ctypes.c_int),
+                ("splits", ctypes.c_int), ("workgroups", ctypes.c_longlong),
+                ("pre_launches", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
 
 _lib = None
 
@@ -54,9 +65,16 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise AttnError(f"{LIB_PATH} is not built; run python scaled_dot_product_amd/build.py")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path: str):
+    """A separate handle on a build of the library at ``path`` with every entry
+    point declared (``using`` routes this module's calls through it)."""
+    if not os.path.exists(path):
+        raise AttnError(f"{path} is not built; run python scaled_dot_product_amd/build.py")
+    lib = ctypes.CDLL(path)
     i, f, vp, sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_fwd.restype = i
@@ -82,12 +100,28 @@ def load_library():
     lib.attn_decode_kvq.restype = i
     lib.attn_decode_kvq_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i]
     lib.attn_decode_kvq_workspace_bytes.restype = sz
+    lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_fwd_decode.restype = i
+    lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
+    lib.attn_fwd_decode_workspace_bytes.restype = sz
+    lib.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.attn_fwd_plan.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
-    lib.attn_probe_mfma.argtypes = [i, i, i, vp, vp]
-    lib.attn_probe_mfma.restype = i
-    _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using(lib):
+    """Route this module's calls through ``lib`` (a handle from open_library)
+    inside the block: two builds can be timed in one process."""
+    global _lib
+    saved = load_library()
+    _lib = lib
+    try:
+        yield lib
+    finally:
+        _lib = saved
 
 
 def _check(status: int, what: str):
@@ -218,9 +252,17 @@ def fwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope: Rope, *, c
 def quantize_qk(q: torch.Tensor, k: torch.Tensor):
     """Per-64-token-block INT8 codes + fp32 scales of Q and K (bf16/f16 input)."""
     lib = load_library()
-    _dev(q, "q"), _dev(k, "k")
+    if q.dim() != 4 or k.dim() != 4:
+        raise AttnError("expected q [B,Hq,Nq,D] and k [B,Hkv,Nk,D]")
+    if q.dtype != k.dtype or q.dtype not in (torch.float16, torch.bfloat16):
+        raise AttnError("q and k must share one dtype, float16 or bfloat16")
     B, Hq, Nq, D = q.shape
-    _, Hkv, Nk, _ = k.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise AttnError("q and k disagree on B or D")
+    if Hq % Hkv != 0:
+        raise AttnError("Hq must be a multiple of Hkv")
+    _dev(q, "q"), _dev(k, "k")
     qc = torch.empty(q.shape, dtype=torch.int8, device=q.device)
     kc = torch.empty(k.shape, dtype=torch.int8, device=k.device)
     qs = torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32, device=q.device)
@@ -236,6 +278,8 @@ def quantize_v(v: torch.Tensor):
     """Per-64-token-block E4M3 codes (uint8) + fp32 scales of V (bf16/f16 input)."""
     lib = load_library()
     _dev(v, "v")
+    if v.dim() != 4:
+        raise AttnError("expected v [B,Hkv,Nk,D]")
     B, Hkv, Nk, D = v.shape
     vc = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     vs = torch.empty((B, Hkv, (Nk + 63) // 64), dtype=torch.float32, device=v.device)
@@ -251,6 +295,8 @@ def quantize_mx(x: torch.Tensor, axis: int = 0):
     channels), axis 1 -> scales [B, H, ceil(N/32), D] (blocks of 32 tokens)."""
     lib = load_library()
     _dev(x, "x")
+    if x.dim() != 4:
+        raise AttnError("expected x [B,H,N,D]")
     B, H, N, D = x.shape
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     sshape = (B, H, N, D // 32) if axis == 0 else (B, H, (N + 31) // 32, D)
@@ -315,13 +361,39 @@ def decode_kvq(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
     return out
 
 
-def probe_mfma(kind: int, iters: int, blocks: int, out: torch.Tensor) -> None:
-    """Matrix-core rate probe on the current stream (measurement only): blocks
-    workgroups of 4 waves, each wave iters * 16 MFMAs of the given kind (0 bf16
-    32x32x16, 1 int8 32x32x32, 2 fp8 32x32x64); out: float32 device tensor of
-    blocks * 256 elements."""
+def fwd_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos0=0,
+                               dtype=torch.float16, splits=0) -> int:
+    return int(load_library().attn_fwd_decode_workspace_bytes(
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), _DTYPE[dtype],
+        int(splits)))
+
+
+def fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, window_lo=0,
+               pos0=0, scale=None, splits=0, out=None, workspace=None) -> torch.Tensor:
+    """The split-KV decode kernel with at most ``splits`` workgroups per KV head
+    (0 = the library's plan), for (Hq / Hkv) * Nq <= 32 whatever the key count."""
     lib = load_library()
-    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * 256:
-        raise AttnError("probe_mfma: out must be a float32 device tensor of blocks * 256 elements")
-    _check(lib.attn_probe_mfma(int(kind), int(iters), int(blocks), ctypes.c_void_p(out.data_ptr()),
-                               _stream_handle(out)), "attn_probe_mfma")
+    B, Hq, Hkv, Nq, Nk, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fwd_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal=causal, window_lo=window_lo,
+                                      pos0=pos0, dtype=q.dtype, splits=splits)
+    out, ws_ptr, ws_len = _out_and_workspace(q, out, workspace, need)
+    st = lib.attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo), int(pos0),
+                             float(scale), _DTYPE[q.dtype], int(splits), ws_ptr, ws_len,
+                             _stream_handle(q))
+    _check(st, "attn_fwd_decode")
+    return out
+
+
+def plan(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, window=0, pos0=0,
+         mode=MODE_EXACT, dtype=torch.bfloat16, rope=False) -> Plan:
+    """The kernels attn_fwd (window > 0: attn_fwd_sliding; rope: attn_fwd_rope)
+    would launch for these sizes (host only)."""
+    p = Plan()
+    st = load_library().attn_fwd_plan(B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo),
+                                      int(window), int(pos0), int(mode), _DTYPE[dtype],
+                                      int(bool(rope)), ctypes.byref(p))
+    _check(st, "attn_fwd_plan")
+    return p

@@ -89,7 +89,9 @@ struct Layout {
   DecodePlan plan{};
 };
 
-Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
+// force_decode >= 0: the decode kernel with that split request (0 = the
+// library's own plan), whatever the key count; -1: attn_fwd's dispatch.
+Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1) {
   Layout L;
   size_t off = 0;
   const size_t nq = (size_t)a.B * a.Hq * a.Nq * a.D;
@@ -123,9 +125,9 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype) {
   } else if (a.rope.on) {
     L.rk = off; off = round_up(off + nk * 2);   // fp32 inputs rotate their bf16 copy in place
   }
-  if (decode_eligible(a)) {
+  if (force_decode >= 0 || decode_eligible(a)) {
     L.decode = true;
-    L.plan = decode_plan(a);
+    L.plan = decode_plan(a, force_decode > 0 ? force_decode : 0);
     L.dec = off; off = round_up(off + L.plan.ws_bytes);
   }
   L.total = off;
@@ -181,10 +183,10 @@ int make_rope(const attn_rope* p, int D, RopeArgs* r, double* logit_mult) {
 
 // One validated forward call: workspace check and kernel dispatch.
 int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, int force_decode = -1) {
   const int B = a.B, Hq = a.Hq, Hkv = a.Hkv, Nq = a.Nq, Nk = a.Nk, D = a.D;
   const void *q = a.q, *k = a.k, *v = a.v;
-  const Layout L = plan_layout(a, mode, dtype);
+  const Layout L = plan_layout(a, mode, dtype, force_decode);
   if (L.total > 0) {
     if (workspace_bytes < L.total) return ATTN_E_WORKSPACE;
     if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) != 0) return ATTN_E_INVALID;
@@ -407,13 +409,66 @@ int attn_decode_kvq(const void* q, const int8_t* k_codes, const float* k_scales,
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
-int attn_probe_mfma(int kind, int iters, int blocks, float* out, void* stream) {
-  if (out == nullptr || !aligned16(out) || kind < 0 || kind > 2 || iters < 1 || blocks < 1 ||
-      blocks > 65535)
-    return ATTN_E_INVALID;
-  return attn::launch_probe_mfma(kind, iters, blocks, out, (hipStream_t)stream) == hipSuccess
-             ? ATTN_OK
-             : ATTN_E_HIP;
+size_t attn_fwd_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                                       int window_lo, int pos0, int dtype, int splits) {
+  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, ATTN_MODE_EXACT, dtype) !=
+          ATTN_OK ||
+      splits < 0)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  if (!decode_supported(a)) return 0;
+  return plan_layout(a, ATTN_MODE_EXACT, dtype, splits).total;
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale,
+                    int dtype, int splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, ATTN_MODE_EXACT, dtype);
+  if (st != ATTN_OK) return st;
+  if (splits < 0) return ATTN_E_INVALID;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
+  if (!decode_supported(a)) return ATTN_E_UNSUPPORTED;
+  return fwd_dispatch(a, ATTN_MODE_EXACT, dtype, workspace, workspace_bytes, stream, splits);
+}
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int window_lo,
+                  int window, int pos0, int mode, int dtype, int rope, attn_plan* plan) {
+  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (window < 0 || (window > 0 && window_lo != 0) || !plan) return ATTN_E_INVALID;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  a.window_w = window;
+  a.rope.on = rope ? 1 : 0;
+  const Layout L = plan_layout(a, mode, dtype);
+  attn_plan p;
+  p.workspace_bytes = L.total;
+  p.splits = 1;
+  if (mode == ATTN_MODE_QUANT || mode == ATTN_MODE_MX) {
+    p.kernel = mode == ATTN_MODE_QUANT ? ATTN_KERNEL_PREFILL_QUANT : ATTN_KERNEL_PREFILL_MX;
+    p.waves = 4;
+    p.rows = 128;
+    p.workgroups = (long long)B * Hq * ((Nq + 127) / 128);
+    p.pre_launches = 3;   // INT8 Q, INT8 K (rotated there with RoPE), V codes
+  } else if (L.decode) {
+    p.kernel = ATTN_KERNEL_DECODE;
+    p.waves = L.plan.waves;
+    p.rows = L.plan.rows;
+    p.splits = L.plan.nsplit;
+    p.workgroups = (long long)L.plan.nsplit * B * Hkv;
+    p.pre_launches = (dtype == ATTN_DT_F32 ? 3 : 0) + (rope ? 1 : 0);
+  } else {
+    p.kernel = ATTN_KERNEL_PREFILL;
+    p.waves = prefill_waves(a);
+    p.rows = 32 * p.waves;
+    p.workgroups = (long long)B * Hq * ((Nq + p.rows - 1) / p.rows);
+    p.pre_launches = (dtype == ATTN_DT_F32 ? 3 : 0) + (rope ? 1 : 0);
+  }
+  *plan = p;
+  return ATTN_OK;
 }
 
 const char* attn_status_string(int status) {

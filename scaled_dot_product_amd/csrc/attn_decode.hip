@@ -25,7 +25,8 @@ namespace attn {
 
 namespace {
 
-constexpr int kMaxSplits = 32;     // workgroups per key/value head, at most
+constexpr int kMaxSplits = 32;     // workgroups per key/value head in the library's plan
+constexpr int kMaxRequestedSplits = 64;   // ... and when the caller chooses
 
 struct DecodeArgs {
   int rows, t_lo, t_hi, nsplit, tiles_per_wg;
@@ -833,29 +834,41 @@ hipError_t launch_kvq_t(const FwdArgs& a, const DecodePlan& pl, const int8_t* kc
 
 }  // namespace
 
-bool decode_eligible(const FwdArgs& a) {
-  const int rows = (a.Hq / a.Hkv) * a.Nq;
-  const KeyRange r = key_range(a);
-  return rows <= 32 && r.hi - r.lo >= 512;
+bool decode_supported(const FwdArgs& a) {
+  return (int64_t)(a.Hq / a.Hkv) * a.Nq <= 32 && (int64_t)a.B * a.Hkv <= 65535;
 }
 
-DecodePlan decode_plan(const FwdArgs& a) {
+bool decode_eligible(const FwdArgs& a) {
+  const KeyRange r = key_range(a);
+  return decode_supported(a) && r.hi - r.lo >= 512;
+}
+
+DecodePlan decode_plan(const FwdArgs& a, int splits) {
   DecodePlan p;
   const KeyRange r = key_range(a);
   p.rows = (a.Hq / a.Hkv) * a.Nq;
   p.t_lo = r.lo / 64;
   const int t_hi = r.hi > r.lo ? (r.hi + 63) / 64 : p.t_lo;
   p.ntiles = t_hi - p.t_lo;
-  // Four waves (one 64-key tile each) per workgroup and at most kMaxSplits
-  // workgroups per key/value head; longer ranges give each wave several
-  // tiles. Fewer, fuller workgroups keep the final merge (on the critical
-  // path, in the last workgroup) short.
-  p.waves = 4;
-  // Up to two tiles per wave, 16 splits merge faster than 32 splits run a
-  // second tile: 32 only for longer ranges.
-  const int cap = p.ntiles <= 2 * p.waves * 16 ? 16 : kMaxSplits;
-  const int per_wave = (p.ntiles + p.waves * cap - 1) / (p.waves * cap);
-  p.tiles_per_wg = p.waves * (per_wave < 1 ? 1 : per_wave);
+  if (splits > 0) {
+    // At most `splits` workgroups, each a contiguous range of tiles, with up
+    // to four waves (one tile each per step).
+    const int ns = splits < kMaxRequestedSplits ? splits : kMaxRequestedSplits;
+    const int per = p.ntiles > 0 ? (p.ntiles + ns - 1) / ns : 1;
+    p.waves = per >= 4 ? 4 : (per >= 2 ? 2 : 1);
+    p.tiles_per_wg = per;
+  } else {
+    // Four waves (one 64-key tile each) per workgroup and at most kMaxSplits
+    // workgroups per key/value head; longer ranges give each wave several
+    // tiles. Fewer, fuller workgroups keep the final merge (on the critical
+    // path, in the last workgroup) short.
+    p.waves = 4;
+    // Up to two tiles per wave, 16 splits merge faster than 32 splits run a
+    // second tile: 32 only for longer ranges.
+    const int cap = p.ntiles <= 2 * p.waves * 16 ? 16 : kMaxSplits;
+    const int per_wave = (p.ntiles + p.waves * cap - 1) / (p.waves * cap);
+    p.tiles_per_wg = p.waves * (per_wave < 1 ? 1 : per_wave);
+  }
   p.nsplit = (p.ntiles + p.tiles_per_wg - 1) / p.tiles_per_wg;
   if (p.nsplit < 1) p.nsplit = 1;
   const size_t nrow = (size_t)a.B * a.Hkv * p.nsplit * p.rows;

@@ -43,6 +43,8 @@ KeyRange key_range(const FwdArgs& a);
 // ---- exact-mode prefill (bf16/f16 MFMA) ----------------------------------
 // elem: 1 = f16, 2 = bf16 operands; out_f32: write fp32 output.
 hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s);
+// Waves (of 32 query rows each) per prefill workgroup for this call: 4 or 8.
+int prefill_waves(const FwdArgs& a);
 
 // ---- split-KV decode + log-sum-exp merge ---------------------------------
 struct DecodePlan {
@@ -55,8 +57,12 @@ struct DecodePlan {
   size_t ctr_bytes;  // arrival counters at the start of the workspace
   size_t ws_bytes;
 };
+// The decode kernel packs G * Nq <= 32 rows and puts B * Hkv on grid.y.
+bool decode_supported(const FwdArgs& a);
+// attn_fwd takes the decode kernel for supported shapes with >= 512 visible keys.
 bool decode_eligible(const FwdArgs& a);
-DecodePlan decode_plan(const FwdArgs& a);
+// splits: 0 = the library's plan, else at most this many workgroups per head.
+DecodePlan decode_plan(const FwdArgs& a, int splits = 0);
 hipError_t launch_decode(const FwdArgs& a, const DecodePlan& p, int elem, bool out_f32,
                          void* ws, hipStream_t s);
 
@@ -98,7 +104,5 @@ hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs
                              const int8_t* kc, const float* ks, const uint8_t* vct,
                              const uint8_t* vs, int elem_out, hipStream_t s);
 
-// Matrix-core rate probe (attn_probe.hip).
-hipError_t launch_probe_mfma(int kind, int iters, int blocks, float* out, hipStream_t s);
 
 }  // namespace attn

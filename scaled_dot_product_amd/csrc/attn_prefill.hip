@@ -432,18 +432,22 @@ hipError_t launch_w(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Eight waves (256 query rows) per workgroup halve the direct-load traffic
-// into LDS per flop, but one such workgroup fills a CU, so the last round of
-// workgroups runs the machine partly idle: they are used only for head dim
-// 128 when the grid is at least eight rounds of 256 workgroups.
 template <typename T, typename TO, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  const int64_t grid8 = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256);
-  if (D == 128 && grid8 >= 8 * 256) return launch_w<T, TO, D, 8>(a, s);
+  if (prefill_waves(a) == 8) return launch_w<T, TO, D, 8>(a, s);
   return launch_w<T, TO, D, 4>(a, s);
 }
 
 }  // namespace
+
+// Eight waves (256 query rows) per workgroup halve the direct-load traffic
+// into LDS per flop, but one such workgroup fills a CU, so the last round of
+// workgroups runs the machine partly idle: they are used only for head dim
+// 128 when the grid is at least eight rounds of 256 workgroups.
+int prefill_waves(const FwdArgs& a) {
+  const int64_t grid8 = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256);
+  return a.D == 128 && grid8 >= 8 * 256 ? 8 : 4;
+}
 
 hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s) {
   if (elem == 2) {

@@ -1,10 +1,18 @@
-// attn_probe.hip — matrix-core rate probe for the measurement report.
+// attn_probe.hip — measurement probes (libattn_probe.so, include/attn_probe.h).
 //
-// Every wave runs a fixed number of MFMAs with register operands (no memory
-// traffic, no vector work) on four independent accumulators, so the launch
-// measures what the matrix cores of this part sustain at its clock under that
-// load: the "measured achievable" figure printed beside the data-sheet peak.
-// Not part of the attention path.
+// Not part of the attention path: these kernels measure what this part
+// sustains, the "measured achievable" figures printed beside the data-sheet
+// peaks, and the floors a short kernel cannot go below.
+//   attn_probe_mfma   matrix cores with register operands only (no memory
+//                     traffic, no vector work), four independent accumulators
+//   attn_probe_read   a bare streaming read of n bytes (16 bytes per lane,
+//                     four loads in flight per lane), the floor of a
+//                     bandwidth-bound kernel of that size
+//   attn_probe_empty  a launch that does nothing, the floor of any kernel
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn_probe.h"
 #include "attn_common.hpp"
 
 namespace attn {
@@ -67,16 +75,68 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(float* out, int iters) 
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
-}  // namespace
-
-hipError_t launch_probe_mfma(int kind, int iters, int blocks, float* out, hipStream_t s) {
-  if (kind == 0)
-    hipLaunchKernelGGL((probe_mfma_kernel<0>), dim3(blocks), dim3(256), 0, s, out, iters);
-  else if (kind == 1)
-    hipLaunchKernelGGL((probe_mfma_kernel<1>), dim3(blocks), dim3(256), 0, s, out, iters);
-  else
-    hipLaunchKernelGGL((probe_mfma_kernel<2>), dim3(blocks), dim3(256), 0, s, out, iters);
-  return hipGetLastError();
+// Each lane reads 16-byte chunks with a grid stride, four in flight, and folds
+// them into one word so the loads cannot be dropped; one word per workgroup
+// is written. n16: number of 16-byte chunks.
+__global__ void __launch_bounds__(256) probe_read_kernel(const u32x4* __restrict__ x, int64_t n16,
+                                                         uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    acc ^= (a[0] ^ a[1] ^ a[2] ^ a[3]) + (b[0] ^ b[1] ^ b[2] ^ b[3]) +
+           (c[0] ^ c[1] ^ c[2] ^ c[3]) + (d[0] ^ d[1] ^ d[2] ^ d[3]);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = x[i];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int t = 0; t < 256; ++t) r ^= red[t];
+    out[blockIdx.x] = r;
+  }
 }
 
+__global__ void probe_empty_kernel() {}
+
+}  // namespace
+
 }  // namespace attn
+
+extern "C" {
+
+int attn_probe_mfma(int kind, int iters, int blocks, float* out, void* stream) {
+  if (out == nullptr || ((uintptr_t)out & 15u) || kind < 0 || kind > 2 || iters < 1 || blocks < 1 ||
+      blocks > 65535)
+    return -1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (kind == 0)
+    hipLaunchKernelGGL((attn::probe_mfma_kernel<0>), dim3(blocks), dim3(256), 0, s, out, iters);
+  else if (kind == 1)
+    hipLaunchKernelGGL((attn::probe_mfma_kernel<1>), dim3(blocks), dim3(256), 0, s, out, iters);
+  else
+    hipLaunchKernelGGL((attn::probe_mfma_kernel<2>), dim3(blocks), dim3(256), 0, s, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int attn_probe_read(const void* x, size_t nbytes, int blocks, uint32_t* out, void* stream) {
+  if (x == nullptr || out == nullptr || ((uintptr_t)x & 15u) || ((uintptr_t)out & 3u) ||
+      (nbytes & 15u) || nbytes == 0 || blocks < 1 || blocks > 65535)
+    return -1;
+  hipLaunchKernelGGL(attn::probe_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const attn::u32x4*)x, (int64_t)(nbytes / 16), out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int attn_probe_empty(int blocks, void* stream) {
+  if (blocks < 1 || blocks > 65535) return -1;
+  hipLaunchKernelGGL(attn::probe_empty_kernel, dim3(blocks), dim3(64), 0, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

@@ -1,6 +1,7 @@
-"""The C-ABI library loads and exports every entry point include/attn.h
-declares; argument checks reject bad calls before touching the GPU (CPU only:
-no compute call is made)."""
+"""The C-ABI libraries load and export every entry point include/attn.h and
+include/attn_probe.h declare; argument checks reject bad calls before touching
+the GPU; the dispatch policy (which kernel each workload takes) is fixed (CPU
+only: no compute call is made)."""
 import ctypes
 import os
 import re
@@ -11,22 +12,34 @@ import scaled_dot_product_amd as sdpa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE = 0, -1, -2, -3
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(sdpa.LIB_PATH):
-        from scaled_dot_product_amd import build
+    from scaled_dot_product_amd import build
+    if not os.path.exists(sdpa.LIB_PATH) or not os.path.exists(build.PROBE_LIB):
         build.build()
     return sdpa.load_library()
+
+
+@pytest.fixture(scope="module")
+def probe(lib):
+    from scaled_dot_product_amd import build
+    p = ctypes.CDLL(build.PROBE_LIB)
+    p.attn_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    p.attn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    p.attn_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    return p
 
 
 def test_header_declares_the_boundary():
@@ -34,14 +47,20 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
               "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
-              "attn_fwd_rope", "attn_fwd_rope_workspace_bytes",
-              "attn_status_string", "attn_probe_mfma"):
+              "attn_fwd_rope", "attn_fwd_rope_workspace_bytes", "attn_fwd_decode",
+              "attn_fwd_decode_workspace_bytes", "attn_fwd_plan", "attn_status_string"):
         assert n in names
+    assert "attn_probe_mfma" not in names     # measurement probes live in their own library
+    assert _declared_functions(PROBE_HEADER) == ["attn_probe_empty", "attn_probe_mfma",
+                                                 "attn_probe_read"]
 
 
-def test_library_exports_every_declared_symbol(lib):
+def test_library_exports_every_declared_symbol(lib, probe):
     for name in _declared_functions():
         assert hasattr(lib, name), name
+    for name in _declared_functions(PROBE_HEADER):
+        assert hasattr(probe, name), name
+    assert not hasattr(lib, "attn_probe_mfma")
 
 
 def test_status_strings(lib):
@@ -204,14 +223,22 @@ def test_sliding_workspace_bytes(lib):
 
 
 
-def test_probe_rejects_before_enqueue(lib):
-    p = lib.attn_probe_mfma
+def test_probe_rejects_before_enqueue(probe):
+    p = probe.attn_probe_mfma
     assert p(0, 4, 2, None, None) == E_INVALID          # no output buffer
     assert p(0, 4, 2, FAKE + 4, None) == E_INVALID      # misaligned
     assert p(3, 4, 2, FAKE, None) == E_INVALID          # unknown kind
     assert p(0, 0, 2, FAKE, None) == E_INVALID          # no iterations
     assert p(1, 4, 0, FAKE, None) == E_INVALID          # no workgroups
     assert p(2, 4, 65536, FAKE, None) == E_INVALID      # grid too large
+    r = probe.attn_probe_read
+    assert r(None, 1024, 4, FAKE, None) == E_INVALID
+    assert r(FAKE + 8, 1024, 4, FAKE, None) == E_INVALID    # misaligned source
+    assert r(FAKE, 1000, 4, FAKE, None) == E_INVALID        # not whole 16-byte chunks
+    assert r(FAKE, 0, 4, FAKE, None) == E_INVALID
+    assert r(FAKE, 1024, 0, FAKE, None) == E_INVALID
+    assert probe.attn_probe_empty(0, None) == E_INVALID
+    assert probe.attn_probe_empty(70000, None) == E_INVALID
 
 
 def test_mx_entry_points_reject_before_enqueue(lib):
@@ -255,3 +282,132 @@ def test_rope_workspace_bytes(lib):
     assert ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 0, 2) >= 40 * 32760 * 128 * 2
     assert ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 0, 2) < 2 * 40 * 32760 * 128 * 2
     assert ws(1, 3, 2, 8, 8, 64, 0, 0, 0, 0, 2) == 0    # rejected shape
+
+
+# ---- split-count decode entry point ----------------------------------------
+
+def _dec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=16, Hkv=8, Nq=4, Nk=4096, D=128,
+             causal=1, window_lo=0, pos0=4092, scale=0.088, dtype=1, splits=0,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_decode(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                               a["Nq"], a["Nk"], a["D"], a["causal"], a["window_lo"], a["pos0"],
+                               a["scale"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(splits=-1), E_INVALID),
+    (dict(q=None), E_INVALID),
+    (dict(v=FAKE + 2), E_INVALID),
+    (dict(ws=FAKE + 16), E_INVALID),
+    (dict(ws_bytes=100), E_WORKSPACE),
+    (dict(Nq=5), E_UNSUPPORTED),                         # 2 x 5 = 10 rows: fine ...
+    (dict(Nq=17), E_UNSUPPORTED),                        # ... 34 rows per KV head are not
+    (dict(B=70000, Hq=2, Hkv=1, Nq=1), E_UNSUPPORTED),   # more than 65535 KV heads
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(scale=0.0), E_INVALID),
+])
+def test_decode_entry_rejects_before_enqueue(lib, kw, want):
+    if kw == dict(Nq=5):
+        # 10 rows fit: this call only fails on the fake workspace size check
+        assert _dec(lib, Nq=5, ws_bytes=64) == E_WORKSPACE
+        return
+    assert _dec(lib, **kw) == want
+
+
+def test_decode_entry_workspace_grows_with_splits(lib):
+    ws = lib.attn_fwd_decode_workspace_bytes
+    args = (1, 16, 8, 4, 4096, 128, 1, 0, 4092, 1)
+    one, lib_plan, many = ws(*args, 1), ws(*args, 0), ws(*args, 32)
+    # counters + per split and packed row: D + 2 fp32 values
+    assert one >= 8 * 8 * 130 * 4
+    assert one < lib_plan < many
+    assert many >= 32 * 8 * 8 * 130 * 4
+    assert ws(*args, 1000) == ws(*args, 64)              # at most one split per 64-key tile ...
+    assert ws(1, 16, 8, 4, 100, 128, 1, 0, 96, 1, 64) == ws(1, 16, 8, 4, 100, 128, 1, 0, 96, 1, 2)
+    assert ws(*args, -1) == 0
+    assert ws(1, 16, 8, 17, 4096, 128, 1, 0, 4092, 1, 0) == 0
+
+
+# ---- dispatch policy -----------------------------------------------------------
+
+def _plan(**kw):
+    import torch
+    dt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[kw.pop("dtype", 2)]
+    args = [kw.pop(k) for k in ("B", "Hq", "Hkv", "Nq", "Nk", "D")]
+    return sdpa.plan(*args, dtype=dt, **kw)
+
+
+def test_dispatch_of_the_five_workloads(lib):
+    from scaled_dot_product_amd.inputs import WORKLOADS
+    import torch
+    want = {
+        # name: (kernel, waves, rows, splits, workgroups, pre_launches)
+        "tiny_fp32_256": (sdpa.KERNEL_PREFILL, 4, 128, 1, 4, 3),
+        "gqa_decode_f16_4096": (sdpa.KERNEL_DECODE, 4, 8, 16, 128, 0),
+        "sdxl_1024px_bf16": (sdpa.KERNEL_PREFILL, 4, 128, 1, 640, 0),
+        "video_dit_bf16_32760": (sdpa.KERNEL_PREFILL, 8, 256, 1, 5120, 0),
+        "video_dit_quant_32760": (sdpa.KERNEL_PREFILL_QUANT, 4, 128, 1, 10240, 3),
+    }
+    for name, exp in want.items():
+        w = WORKLOADS[name]
+        p = sdpa.plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal, window_lo=w.window_lo,
+                      pos0=w.pos0, mode=w.mode, dtype=w.dtype)
+        got = (p.kernel, p.waves, p.rows, p.splits, p.workgroups, p.pre_launches)
+        assert got == exp, (name, got)
+        assert p.workspace_bytes == sdpa.fwd_workspace_bytes(
+            w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal, window_lo=w.window_lo,
+            pos0=w.pos0, mode=w.mode, dtype=w.dtype)
+    # the window variant of the decode shape still decodes, over fewer tiles
+    p = sdpa.plan(1, 16, 8, 4, 4096, 128, causal=True, window_lo=1000, pos0=4092,
+                  dtype=torch.float16)
+    assert p.kernel == sdpa.KERNEL_DECODE and p.splits == 13
+
+
+def test_dispatch_boundaries(lib):
+    import torch
+    f16 = torch.float16
+    # 32 packed rows decode, 34 do not
+    assert _plan(B=1, Hq=8, Hkv=1, Nq=4, Nk=4096, D=128, dtype=1).kernel == sdpa.KERNEL_DECODE
+    assert _plan(B=1, Hq=2, Hkv=1, Nq=17, Nk=4096, D=128, dtype=1).kernel == sdpa.KERNEL_PREFILL
+    # fewer than 512 visible keys go to the prefill
+    assert _plan(B=1, Hq=2, Hkv=1, Nq=1, Nk=511, D=128, dtype=1).kernel == sdpa.KERNEL_PREFILL
+    assert _plan(B=1, Hq=2, Hkv=1, Nq=1, Nk=512, D=128, dtype=1).kernel == sdpa.KERNEL_DECODE
+    # more than 65535 key/value heads cannot sit on the decode grid's y axis: prefill
+    p = _plan(B=70000, Hq=2, Hkv=1, Nq=1, Nk=4096, D=128, dtype=1)
+    assert p.kernel == sdpa.KERNEL_PREFILL and p.workspace_bytes == 0
+    p = _plan(B=65535, Hq=2, Hkv=1, Nq=1, Nk=4096, D=128, dtype=1)
+    assert p.kernel == sdpa.KERNEL_DECODE
+    assert sdpa.fwd_workspace_bytes(70000, 2, 1, 1, 4096, 128, dtype=f16) == 0
+    # eight-wave prefill only for head dim 128 and grids of >= 8 rounds of 256 workgroups
+    assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=128).waves == 8
+    assert _plan(B=1, Hq=63, Hkv=63, Nq=8192, Nk=8192, D=128).waves == 4
+    assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=64).waves == 4
+    # the MX mode, RoPE's extra pass and fp32 staging
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, mode=2).kernel == sdpa.KERNEL_PREFILL_MX
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, rope=True).pre_launches == 1
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, dtype=0, rope=True).pre_launches == 4
+    # a per-row window: the decode over the window's tiles
+    p = _plan(B=1, Hq=16, Hkv=8, Nq=4, Nk=4096, D=128, dtype=1, causal=True, pos0=4092,
+              window=1024)
+    assert p.kernel == sdpa.KERNEL_DECODE
+    with pytest.raises(sdpa.AttnError):
+        _plan(B=1, Hq=3, Hkv=2, Nq=4, Nk=4096, D=128)
+
+
+def test_binding_quantize_qk_checks_pair_before_launch():
+    # mismatched q, k pairs are refused before any device pointer is taken
+    import torch
+    q = torch.zeros(1, 4, 64, 128, dtype=torch.bfloat16)
+    for k, what in ((torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16), "D"),
+                    (torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16), "B"),
+                    (torch.zeros(1, 3, 64, 128, dtype=torch.bfloat16), "Hq % Hkv"),
+                    (torch.zeros(1, 2, 64, 128, dtype=torch.float16), "dtype"),
+                    (torch.zeros(2, 64, 128, dtype=torch.bfloat16), "rank")):
+        with pytest.raises(sdpa.AttnError) as e:
+            sdpa.quantize_qk(q, k)
+        assert "device" not in str(e.value), what
+    with pytest.raises(sdpa.AttnError, match="device"):
+        sdpa.quantize_qk(q, torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16))

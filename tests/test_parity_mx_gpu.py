@@ -95,11 +95,26 @@ def test_mx_mode_sliding_window():
 
 
 def test_mx_mode_video_dit_sampled():
-    # against exact attention only: the oracle's MX dequantisation of the
-    # full-size K and V (one brute-force E4M3 encode per element) would take
-    # minutes on the host
+    # against exact attention on 128 sampled rows of every head, and against
+    # the MX reference on two whole heads' samples: MX blocks never cross a
+    # head, so the oracle's MX dequantisation of one head's K and V (a
+    # brute-force E4M3 encode per element) is that head's slice of the full one
     w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_mx_32760", mode=2)
-    _check(w, rows=sample_rows(w, 128), mx_ref=False)
+    q, k, v = make_qkv(w)
+    out = _check(w, rows=sample_rows(w, 128), inputs=(q, k, v), mx_ref=False)
+    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0)
+    rng = np.random.default_rng(5)
+    for h in (0, 39):
+        announce(f"mx video head {h} against the MX reference")
+        rows = np.unique(np.concatenate([rng.choice(w.Nq, 62, replace=False),
+                                         np.array([0, w.Nq - 1])])).astype(np.int64)
+        sl = (slice(None), slice(h, h + 1))
+        ref_mx = oracle.attn_mx(q[sl].contiguous(), k[sl].contiguous(), v[sl].contiguous(),
+                                rows=rows, **kw)
+        got = out[0, h].numpy()[rows]
+        rel_mx, _ = metrics(got, ref_mx)
+        print(f"    head {h}: rel(vs MX-dequantised inputs)={rel_mx:.3e}", flush=True)
+        assert rel_mx <= MX_P_REL, rel_mx
 
 
 def test_mx_mode_sdxl_1024px_against_mx_reference():
