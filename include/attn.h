@@ -41,7 +41,9 @@ typedef enum {
   ATTN_E_INVALID = -1,     /* null/misaligned pointer, bad size, bad scale  */
   ATTN_E_UNSUPPORTED = -2, /* head dim, dtype, mode or shape not supported  */
   ATTN_E_WORKSPACE = -3,   /* workspace below the matching *_workspace_bytes */
-  ATTN_E_HIP = -4          /* the HIP runtime refused a launch              */
+  ATTN_E_HIP = -4,         /* the HIP runtime refused a launch              */
+  ATTN_E_TOO_LARGE = -5    /* the call needs more scratch than
+                              attn_fwd_noalloc holds                         */
 } attn_status;
 
 /* Element types of Q, K, V and O. */
@@ -347,6 +349,36 @@ typedef struct {
 
 int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int window_lo,
                   int window, int pos0, int mode, int dtype, int rope, attn_plan* plan);
+
+/*
+ * attn_fwd_noalloc — attn_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It allocates nothing (no hipMalloc, hipFree or allocating
+ * library call): the workspace attn_fwd would need comes from one fixed array
+ * of ATTN_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * every GPU it runs on until the process ends. Its device address is looked
+ * up once per device, on the first call on that device.
+ *
+ * Arguments, layouts, modes and results are those of attn_fwd (the same
+ * kernels run); the caller passes only inputs and outputs. Errors:
+ *   every attn_fwd argument error, checked first (nothing enqueued);
+ *   ATTN_E_TOO_LARGE  attn_fwd_workspace_bytes(...) > ATTN_NOALLOC_SCRATCH_BYTES
+ *                     (e.g. the quantised modes at long sequences, fp32 inputs
+ *                     beyond about 2 M elements);
+ *   ATTN_E_INVALID    `stream` belongs to another device than the current one;
+ *   ATTN_E_HIP        the device address could not be looked up, or a launch
+ *                     failed.
+ * Calls on one GPU share its array, which keeps the last call's contents (no
+ * kernel here needs it cleared: the decode's arrival counters carry a per-call
+ * tag), so calls that overlap on one GPU (different streams, or concurrent host
+ * threads) race and must be serialised by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                     int causal, int window_lo, int pos0, float scale, int mode,
+                     int dtype, void* stream);
 
 /* Static English text for a status code. */
 const char* attn_status_string(int status);

@@ -22,7 +22,7 @@ __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_b
            "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
            "decode_kvq_workspace_bytes", "fwd_decode", "fwd_decode_workspace_bytes", "plan",
            "Plan", "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_PREFILL_QUANT", "KERNEL_PREFILL_MX",
-           "load_library", "open_library", "using",
+           "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "load_library", "open_library", "using",
            "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -34,6 +34,7 @@ _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2
 KERNEL_PREFILL, KERNEL_DECODE, KERNEL_PREFILL_QUANT, KERNEL_PREFILL_MX = 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 16 << 20      # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
 
 
 class Rope(ctypes.Structure):
@@ -104,6 +105,8 @@ def open_library(path: str):
     lib.attn_fwd_decode.restype = i
     lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
     lib.attn_fwd_decode_workspace_bytes.restype = sz
+    lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_noalloc.restype = i
     lib.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.attn_fwd_plan.restype = i
     lib.attn_status_string.argtypes = [i]
@@ -397,3 +400,24 @@ def plan(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, window=0, pos0=0,
                                       int(bool(rope)), ctypes.byref(p))
     _check(st, "attn_fwd_plan")
     return p
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=False, window_lo=0,
+                pos0=0, scale=None, mode=MODE_EXACT, out=None) -> torch.Tensor:
+    """attn_fwd_noalloc: fwd whose workspace is the library's fixed device array
+    (no device allocation by the library; calls that overlap on one GPU race)."""
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise AttnError("out must match q's shape and dtype")
+    st = lib.attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo), int(pos0),
+                              float(scale), int(mode), _DTYPE[q.dtype], _stream_handle(q))
+    _check(st, "attn_fwd_noalloc")
+    return out

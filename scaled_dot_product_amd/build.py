@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 PROBE_LIB = os.path.join(HERE, "libattn_probe.so")
-SOURCES = ["attn_api.cpp", "attn_prefill.hip", "attn_decode.hip",
+SOURCES = ["attn_api.cpp", "attn_noalloc.hip", "attn_prefill.hip", "attn_decode.hip",
            "attn_quant.hip", "attn_mx.hip"]
 PROBE_SOURCES = ["attn_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -256,6 +256,17 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
 }
 
 }  // namespace
+
+int fwd_validate(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
+                 int dtype) {
+  const int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  return ATTN_OK;
+}
+
 }  // namespace attn
 
 using namespace attn;
@@ -274,10 +285,9 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, i
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
              int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
              int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale, mode, dtype);
+  const int st = attn::fwd_validate(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0,
+                                    scale, mode, dtype);
   if (st != ATTN_OK) return st;
-  if (!q || !k || !v || !o) return ATTN_E_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
   FwdArgs a = make_args(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale);
   return fwd_dispatch(a, mode, dtype, workspace, workspace_bytes, stream);
 }
@@ -478,6 +488,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_UNSUPPORTED: return "unsupported head dimension, dtype, mode or shape";
     case ATTN_E_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() result";
     case ATTN_E_HIP: return "the HIP runtime refused a kernel launch";
+    case ATTN_E_TOO_LARGE: return "the call needs more scratch than the allocation-free entry point holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -34,6 +34,12 @@ struct FwdArgs {
   RopeArgs rope;   // rotation of Q in the kernels (K is rotated before them)
 };
 
+// The argument checks of attn_fwd (everything but the workspace): ATTN_OK or
+// the status attn_fwd returns. Host-only, touches no runtime state.
+int fwd_validate(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
+                 int dtype);
+
 // Visible key range [lo, hi) over all rows of a call (hi <= lo: none).
 struct KeyRange {
   int lo, hi;

@@ -48,7 +48,8 @@ def test_header_declares_the_boundary():
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
               "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
               "attn_fwd_rope", "attn_fwd_rope_workspace_bytes", "attn_fwd_decode",
-              "attn_fwd_decode_workspace_bytes", "attn_fwd_plan", "attn_status_string"):
+              "attn_fwd_decode_workspace_bytes", "attn_fwd_plan", "attn_fwd_noalloc",
+              "attn_status_string"):
         assert n in names
     assert "attn_probe_mfma" not in names     # measurement probes live in their own library
     assert _declared_functions(PROBE_HEADER) == ["attn_probe_empty", "attn_probe_mfma",
@@ -64,7 +65,7 @@ def test_library_exports_every_declared_symbol(lib, probe):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.attn_status_string(st), bytes)
 
 
@@ -411,3 +412,39 @@ def test_binding_quantize_qk_checks_pair_before_launch():
         assert "device" not in str(e.value), what
     with pytest.raises(sdpa.AttnError, match="device"):
         sdpa.quantize_qk(q, torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16))
+
+
+# ---- allocation-free entry point: argument and size checks on the host -----------
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=16, Hkv=8, Nq=4, Nk=4096, D=128,
+             causal=1, window_lo=0, pos0=4092, scale=0.088, mode=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                                a["Nq"], a["Nk"], a["D"], a["causal"], a["window_lo"], a["pos0"],
+                                a["scale"], a["mode"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_INVALID),
+    (dict(o=FAKE + 4), E_INVALID),
+    (dict(Hq=12), E_INVALID),
+    (dict(D=80), E_UNSUPPORTED),
+    (dict(mode=1, dtype=0), E_UNSUPPORTED),
+    (dict(scale=float("inf")), E_INVALID),
+    # quantised mode at 8 x 8192 x 128: 25 MB of codes > the 16 MiB array
+    (dict(Hq=8, Hkv=8, Nq=8192, Nk=8192, causal=0, pos0=0, mode=1, dtype=2), -5),
+    # fp32 inputs staged as bf16 copies: 3 x 8 x 4096 x 128 x 2 bytes = 25 MB > 16 MiB
+    (dict(B=1, Hq=8, Hkv=8, Nq=4096, Nk=4096, causal=0, pos0=0, dtype=0), -5),
+])
+def test_noalloc_rejects_before_touching_the_device(lib, kw, want):
+    assert _noalloc(lib, **kw) == want
+
+
+def test_noalloc_scratch_size_covers_the_decode(lib):
+    # the decode workload's partials fit the fixed array many times over
+    need = lib.attn_fwd_workspace_bytes(1, 16, 8, 4, 4096, 128, 1, 0, 4092, 0, 1)
+    assert 0 < need < sdpa.NOALLOC_SCRATCH_BYTES // 8
+    text = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert sdpa.NOALLOC_SCRATCH_BYTES == 16 << 20
