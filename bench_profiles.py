@@ -138,7 +138,8 @@ def cmd_counters(a):
         lst.sort()
         lst = lst[a.skip:] or lst
         for c in lst[0][1]:
-            merged[c] = statistics.median(v[c] for _, v in lst if c in v)
+            if c not in merged:   # a counter repeated in a later pass keeps the first pass's value
+                merged[c] = statistics.median(v[c] for _, v in lst if c in v)
     lines = [f"# {a.title} (counters)", "",
              "Commands (from the repository root on one MI355X, `export TMPDIR=/tmp` first):", "",
              "```"] + a.cmd + ["```", "", "| counter | value (median over the counted dispatches) |",
