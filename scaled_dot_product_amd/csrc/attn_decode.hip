@@ -6,12 +6,14 @@
 // into the 32 columns of one MFMA block, so each K/V byte feeds every one of
 // them. The visible keys are cut into 64-key tiles; each wave streams its own
 // tiles through a private pair of LDS tiles (direct global-to-LDS loads, the
-// prefill's swizzles; V^T operands by transpose reads; the next K tile loads
-// while this one's softmax and P V run) and keeps an online-softmax partial
-// (O_s, m_s, l_s); the waves of a workgroup merge theirs in LDS and publish one
-// partial per workgroup. The last workgroup of a key/value head to publish
-// merges all partials of that head with log-sum-exp weights and writes O, so
-// one kernel launch does the whole decode. This is the chunked attention +
+// prefill's swizzles; V^T operands by transpose reads; a wave's first scores
+// are computed as soon as its K tile lands, while V is still arriving) and
+// keeps an online-softmax partial (O_s, m_s, l_s); the waves of a workgroup
+// merge theirs in LDS and publish one partial per workgroup, O_s normalised by
+// l_s and rounded to the output element type (half the bytes the merging
+// workgroup must read, at the output's own precision). The last workgroup of a
+// key/value head to publish merges all partials of that head with log-sum-exp
+// weights and writes O, so one kernel launch does the whole decode. This is the chunked attention +
 // merge structure of "round 21 track b — qsa2" (partial buffers combined by a
 // merge with cached maxima and weights and a denominator computed once),
 // written for wave64 MFMA and fused into one launch.
@@ -30,7 +32,7 @@ constexpr int kMaxRequestedSplits = 64;   // ... and when the caller chooses
 
 struct DecodeArgs {
   int rows, t_lo, t_hi, nsplit, tiles_per_wg;
-  float* opart;  // [B*Hkv][nsplit][rows][D], unnormalised
+  float* opart;  // [B*Hkv][nsplit][rows][D] of O_s / l_s in the output type (fp32-sized area)
   float* mpart;  // [B*Hkv][nsplit][rows], running max in exp2 units
   float* lpart;  // [B*Hkv][nsplit][rows]
   unsigned long long* ctr;  // [B*Hkv] arrivals: (generation << 24) | count
@@ -39,9 +41,12 @@ struct DecodeArgs {
 
 // Partials cross workgroups that may sit on different XCDs, whose L2 caches
 // are not coherent with each other. They are written and read with
-// agent-scope atomic accesses (write-through / L2-bypassing), so no L2
-// write-back or invalidate is needed; a workgroup counts its arrival only
-// after all its partial stores are acknowledged.
+// agent-scope atomic accesses, and a workgroup counts its arrival only after
+// all its partial stores are acknowledged and its waves have met at a
+// barrier; the arrival is an agent-scope acquire-release add, so the merging
+// workgroup (whose add reads the others') sees every partial by the memory
+// model's happens-before (workgroup barrier, then agent-scope release and
+// acquire), not by a property of this hardware.
 __device__ __forceinline__ void put4(float* dst, f32x4 v) {
   unsigned long long* d = (unsigned long long*)dst;
   const u32x4 u = __builtin_bit_cast(u32x4, v);
@@ -56,6 +61,34 @@ __device__ __forceinline__ f32x4 get4(const float* src) {
   const unsigned long long b = __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const u32x4 u = {(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
   return __builtin_bit_cast(f32x4, u);
+}
+// Four partial values in the output element type: one 64-bit word (16-bit
+// types) or two (fp32).
+template <typename TO>
+__device__ __forceinline__ void put_part(float* base, int64_t idx, f32x4 v) {
+  if constexpr (sizeof(TO) == 2) {
+    TO o4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o4[c] = Elem<TO>::from_float(v[c]);
+    unsigned long long w;
+    __builtin_memcpy(&w, o4, 8);
+    __hip_atomic_store((unsigned long long*)((TO*)base + idx), w, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    put4(base + idx, v);
+  }
+}
+template <typename TO>
+__device__ __forceinline__ f32x4 get_part(const float* base, int64_t idx) {
+  if constexpr (sizeof(TO) == 2) {
+    const unsigned long long w = __hip_atomic_load((unsigned long long*)((const TO*)base + idx),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    TO o4[4];
+    __builtin_memcpy(o4, &w, 8);
+    return f32x4{(float)o4[0], (float)o4[1], (float)o4[2], (float)o4[3]};
+  } else {
+    return get4(base + idx);
+  }
 }
 __device__ __forceinline__ void put1(float* dst, float v) {
   __hip_atomic_store((unsigned*)dst, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -76,7 +109,8 @@ __device__ __forceinline__ float get1(const float* src) {
 // generation) claim it again. Every swap precedes its own workgroup's
 // arrival, so all of them precede the reset.
 __device__ bool arrive_last(unsigned long long* c, int nsplit) {
-  const unsigned long long old = atomicAdd(c, 1ull);
+  const unsigned long long old =
+      __hip_atomic_fetch_add(c, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
   return (int)(old & 0xffffffull) == nsplit - 1;
 }
 
@@ -109,6 +143,7 @@ __device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs
         put1(&p.mpart[pbase + col], m);
         put1(&p.lpart[pbase + col], l);
       }
+      const float r = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -116,8 +151,8 @@ __device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs
           const int d = 32 * db + 8 * a4 + 4 * half;
           f32x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = oacc[db][4 * a4 + r];
-          put4(&p.opart[(pbase + col) * D + d], v);
+          for (int q = 0; q < 4; ++q) v[q] = oacc[db][4 * a4 + q] * r;
+          put_part<TO>(p.opart, (pbase + col) * D + d, v);
         }
     }
   } else {
@@ -160,7 +195,10 @@ __device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs
           for (int r = 0; r < 4; ++r) acc[r] += f * v[r];
         }
       }
-      put4(&p.opart[(pbase + n) * D + d], acc);
+      const float r = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] *= r;
+      put_part<TO>(p.opart, (pbase + n) * D + d, acc);
       if (d == 0) {
         put1(&p.mpart[pbase + n], M);
         put1(&p.lpart[pbase + n], L);
@@ -177,8 +215,9 @@ __device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs
   if (!s_last) return;
 
   // Final merge, one thread per (row, 4 channels): all loads of a chunk of
-  // splits first (one memory round trip per 16 splits), then an online
-  // log-sum-exp merge in registers, in split order.
+  // splits first (one memory round trip per 16 splits), then the chunk's
+  // largest maximum, then its weights 2^(m_s - M) l_s and the weighted sum of
+  // the normalised partials, without branches; chunks combine online.
   constexpr int NT = 64 * kWaves;
   constexpr int SLOTS = D / 4;
   constexpr int CH = 16;
@@ -195,26 +234,28 @@ __device__ __forceinline__ void decode_finish(const FwdArgs& a, const DecodeArgs
       for (int u = 0; u < CH; ++u) {
         const int sp = min(s0 + u, ns - 1);
         const int64_t r = hbase + (int64_t)sp * rows + n;
-        mv[u] = get1(&p.mpart[r]);
+        mv[u] = s0 + u < ns ? get1(&p.mpart[r]) : -INFINITY;
         lv[u] = get1(&p.lpart[r]);
-        ov[u] = get4(&p.opart[r * D + d]);
+        ov[u] = get_part<TO>(p.opart, r * D + d);
       }
+      float Mc = M;
+#pragma unroll
+      for (int u = 0; u < CH; ++u) Mc = fmaxf(Mc, mv[u]);
+      // (no split with a visible key yet: nothing to scale)
+      const float sc = Mc == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mc);
+      L *= sc;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] *= sc;
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
-        if (s0 + u >= ns || mv[u] == -INFINITY) continue;
-        if (mv[u] > M) {
-          const float f = __builtin_amdgcn_exp2f(M - mv[u]);   // 0 while M = -inf
-          L = L * f + lv[u];
+        // a split with no visible key has m = -inf and weight 0
+        const float wgt = __builtin_amdgcn_exp2f(mv[u] - Mc) * lv[u];
+        const float w = mv[u] == -INFINITY ? 0.0f : wgt;
+        L += w;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] = acc[c] * f + ov[u][c];
-          M = mv[u];
-        } else {
-          const float f = __builtin_amdgcn_exp2f(mv[u] - M);
-          L += f * lv[u];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] += f * ov[u][c];
-        }
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, ov[u][c], acc[c]);
       }
+      M = Mc;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int hh2 = n / a.Nq, qi2 = n - hh2 * a.Nq;
@@ -337,9 +378,19 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
   auto tile = [&](int t) {
     const int k0 = t * 64;
     const bool more = t + kWaves < t1;
-    // this wave's K and V tiles (and everything loaded before) have landed;
-    // the direct loads are not tracked by the compiler, so this wait is ours
-    vmem_wait_all();
+    const bool first = t == t0 + wave;
+    // The direct loads are not tracked by the compiler, so these waits are
+    // ours. A wave's first tile: only its K tile has to have landed here (the
+    // NL loads of V were issued after it, and in wave 0 the counter read
+    // after those); later tiles wait for everything issued before.
+    if (first) {
+      if (wave == 0)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+    } else {
+      vmem_wait_all();
+    }
     // S^T = K Q^T: four independent accumulators (even/odd k-steps).
     f32x16 s[2][2];
 #pragma unroll
@@ -409,6 +460,13 @@ decode_kernel(FwdArgs a, DecodeArgs p) {
           pv[mb][tt][i] = E::from_float(e);
         }
     l += halves_sum(lsum);
+    // The first tile's V has landed (a next K tile, if any, was issued after it).
+    if (first) {
+      if (more)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+      else
+        vmem_wait_all();
+    }
     // O^T += V^T P^T; the V^T operands come through transpose reads (as in the
     // prefill): lane r of a 16-lane group names key kb + r/4 at channel d0 + 4 (r % 4).
     const int gq = lane >> 4, rr = lane & 15;
