@@ -16,7 +16,8 @@ figure there can be regenerated from a profiler run of committed files.
                                       --out profiles/x.md [--json profiles/x.json]
 
 `--skip W` drops the first W dispatches of the kernel (warm-up launches), so
-the figures are those of the timed launches only. Timestamps are nanoseconds.
+the figures are those of the timed launches only; `--first N` keeps the N
+dispatches after them (one case of a command that runs several). Timestamps are nanoseconds.
 """
 from __future__ import annotations
 
@@ -87,12 +88,13 @@ def cmd_trace(a):
                      f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     sel = _pick(tr, a.kernel, "traced")
     durs = [(e - s) / 1e3 for _, s, e in sel]
-    timed = durs[a.skip:]
+    timed = durs[a.skip:a.skip + a.first] if a.first else durs[a.skip:]
     if not timed:
         sys.exit("nothing left after --skip")
     mean, med = statistics.mean(timed), statistics.median(timed)
     lines += ["", f"Kernel `{_short(sel[0][0])}`: {len(durs)} dispatches; the first {a.skip} "
-                  f"(warm-up) are dropped.", ""]
+                  f"(warm-up) are dropped" + (f", the {len(timed)} after them are the timed "
+                                              f"launches" if a.first else "") + ".", ""]
     if len(durs) <= 64:
         lines += ["Per-dispatch durations (us): " + ", ".join(f"{x:.1f}" for x in durs) + ".", ""]
     lines += ["| timed launches | value |", "|---|---|",
@@ -188,10 +190,12 @@ def cmd_counters(a):
     _write(a.out, lines)
 
 
-def _median_counter(d, part, counter, skip):
+def _median_counter(d, part, counter, skip, first=0):
     vals = sorted((did, v[counter]) for did, (n, v) in counter_rows(d).items()
                   if part in n and counter in v)
     vals = [x for _, x in vals[skip:]] or [x for _, x in vals]
+    if first:
+        vals = vals[:first]
     if not vals:
         sys.exit(f"no {counter} for {part!r} under {d}")
     return statistics.median(vals), len(vals)
@@ -199,8 +203,8 @@ def _median_counter(d, part, counter, skip):
 
 def cmd_traffic(a):
     copy_part = "copyBuffer"
-    fk, nf = _median_counter(a.fetch, a.kernel, "FETCH_SIZE", a.skip)
-    wk, nw = _median_counter(a.write, a.kernel, "WRITE_SIZE", a.skip)
+    fk, nf = _median_counter(a.fetch, a.kernel, "FETCH_SIZE", a.skip, a.first)
+    wk, nw = _median_counter(a.write, a.kernel, "WRITE_SIZE", a.skip, a.first)
     cf, _ = _median_counter(a.copy_fetch, copy_part, "FETCH_SIZE", 0)
     cw, _ = _median_counter(a.copy_write, copy_part, "WRITE_SIZE", 0)
     gib_kib = (1 << 30) / 1024
@@ -270,6 +274,8 @@ def main():
     for p in (t, c, r):
         p.add_argument("--kernel", required=True)
         p.add_argument("--skip", type=int, default=0)
+        p.add_argument("--first", type=int, default=0,
+                       help="keep only the first N dispatches after --skip")
         p.add_argument("--title", required=True)
         p.add_argument("--cmd", action="append", required=True)
         p.add_argument("--note")
