@@ -65,13 +65,32 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_events(fn, iters, warmup, per_launch=None):
-    """ms per call over iters back-to-back calls (HIP events on the current
-    stream). per_launch: a list that receives each call's own duration (ms)."""
+# Seconds of back-to-back work before any timed region: from idle the part
+# needs tens of milliseconds of load before its clocks settle (a 110 us kernel
+# measured 128 us per call over its first 60 launches and 112 us after 200),
+# so warm-up is counted in time as well as in launches.
+WARM_S = 0.2
+
+
+def _warm(fn, warmup):
+    """Run fn warmup times, then until WARM_S seconds of them have passed."""
     import torch
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < WARM_S:
+        for _ in range(max(warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_events(fn, iters, warmup, per_launch=None):
+    """ms per call over iters back-to-back calls (HIP events on the current
+    stream), after the warm-up of _warm. per_launch: a list that receives each
+    call's own duration (ms)."""
+    import torch
+    _warm(fn, warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)] \
@@ -135,9 +154,10 @@ def bench_quant_prep(w, iters=5):
     return time_events(prep, iters, 2)
 
 
-def bench_decode(w, nbuf=48, reps=20):
+def bench_decode(w, nbuf=48, reps=20, hot=True):
     """Cold-cache decode: nbuf independent KV caches, one call per cache, captured
-    in a HIP graph; returns (us per call cold, us per call hot, bytes per call).
+    in a HIP graph; returns (us per call cold, us per call hot or None, bytes per
+    call).
     w.mode 2: the cache is INT8 K / E4M3 V codes with per-64-key scales."""
     import torch
     import scaled_dot_product_amd as sdpa
@@ -172,9 +192,76 @@ def bench_decode(w, nbuf=48, reps=20):
         call(i)
     torch.cuda.synchronize()
     cold = graph_us_per_call([lambda i=i: call(i) for i in range(nbuf)], reps)
-    hot = graph_us_per_call([lambda: call(0)] * nbuf, reps)
+    hot_us = graph_us_per_call([lambda: call(0)] * nbuf, reps) if hot else None
     del sets, ws
-    return cold, hot, decode_bytes(w)
+    return cold, hot_us, decode_bytes(w)
+
+
+def decode_chunk_sweep(splits_list=(64, 32, 16, 8, 4), rounds=9, reps=20, nbuf=48, seed=1):
+    """Cold decode at gqa_decode_f16_4096 with each split count (keys per
+    partial = 4096 / splits): one graph of nbuf calls over rotated caches per
+    split count, timed in rounds that visit the counts in alternating order
+    (round 0 discarded); per count the median us per call and the bootstrap
+    95 % interval of the mean ratio to the library's own plan (16 splits)."""
+    import numpy as np
+    import torch
+    import scaled_dot_product_amd as sdpa
+    from scaled_dot_product_amd.inputs import WORKLOADS, make_qkv
+    w = WORKLOADS["gqa_decode_f16_4096"]
+    dev = torch.device("cuda:0")
+    q0, k0, v0 = (t.to(dev) for t in make_qkv(w))
+    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nbuf)]
+    graphs = {}
+    for sp in splits_list:
+        need = sdpa.fwd_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                                               window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype,
+                                               splits=sp)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def call(i, sp=sp, ws=ws):
+            q, k, v, o = sets[i]
+            sdpa.fwd_decode(q, k, v, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0,
+                            scale=w.scale, splits=sp, out=o, workspace=ws)
+        for i in range(nbuf):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nbuf):
+                call(i)
+        torch.cuda.synchronize()
+        graphs[sp] = (g, ws)
+    first = splits_list[0]
+    _warm(graphs[first][0].replay, 3)
+    times = {sp: [] for sp in splits_list}
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for r in range(rounds + 1):
+        order = list(splits_list) if r % 2 == 0 else list(reversed(splits_list))
+        for sp in order:
+            g = graphs[sp][0]
+            g.replay()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times[sp].append(e0.elapsed_time(e1) * 1e3 / (reps * nbuf))
+    ref = np.array(times[16][1:]) if 16 in times else np.array(times[first][1:])
+    rng = np.random.default_rng(seed)
+    out = {}
+    for sp in splits_list:
+        t = np.array(times[sp][1:])
+        ratio = t / ref
+        boots = np.array([ratio[rng.integers(0, ratio.size, ratio.size)].mean() for _ in range(4000)])
+        lo, hi = np.percentile(boots, [2.5, 97.5])
+        p = sdpa.plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal, pos0=w.pos0, dtype=w.dtype)
+        out[str(sp)] = {"keys_per_partial": -(-w.Nk // sp), "us_cold_median": round(float(np.median(t)), 3),
+                        "ratio_to_16": round(float(ratio.mean()), 4),
+                        "ci95": [round(float(lo), 4), round(float(hi), 4)]}
+        log(f"decode splits {sp}: {out[str(sp)]}")
+    del sets, graphs
+    return {"workload": w.name, "rounds": rounds, "plan_splits": int(p.splits), "by_splits": out}
 
 
 def decode_bytes(w):
@@ -259,9 +346,7 @@ def graph_us_per_call(calls, reps=20):
         for c in calls:
             c()
     torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
+    _warm(g.replay, 3)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -446,6 +531,15 @@ def run_extra(part):
                               "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1)}
             log(f"decode sweep Nk={nk}: {cold_us:.2f} us, {sweep[str(nk)]['gbs_cold']} GB/s")
         extra["decode_kv_sweep"] = sweep
+    elif part == "decode_chunks":
+        extra["decode_chunks"] = decode_chunk_sweep()
+    elif part in ("decode_cold", "decode_kvq_cold"):
+        # the cold Nk = 4096 case alone (for profiler runs)
+        wd = WORKLOADS["gqa_decode_f16_4096" if part == "decode_cold" else "gqa_decode_kvq_f16_4096"]
+        cold_us, _, nbytes = bench_decode(wd, hot=False)
+        extra[part] = {"workload": wd.name, "us_per_call_cold": round(cold_us, 3),
+                       "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1), "bytes_per_call": nbytes}
+        log(f"{part}: {cold_us:.2f} us ({extra[part]['gbs_cold']} GB/s)")
     elif part == "decode_kvq":
         wk = WORKLOADS["gqa_decode_kvq_f16_4096"]
         cold_us, hot_us, nbytes = bench_decode(wk)
@@ -577,12 +671,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
-    ap.add_argument("--only", choices=["decode", "decode_kvq", "quant", "mx", "rope", "causal",
-                                       "sliding", "sdxl", "copy", "floor"],
+    ap.add_argument("--only", choices=["decode", "decode_kvq", "decode_cold", "decode_kvq_cold",
+                                       "decode_chunks",
+                                       "quant", "mx", "rope", "causal", "sliding", "sdxl", "copy",
+                                       "floor"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters; 'floor' the "
-                         "empty-launch and bare-read floors under the decode")
+                         "empty-launch and bare-read floors under the decode; "
+                         "'decode_cold' / 'decode_kvq_cold' the cold Nk = 4096 decode alone; "
+                         "'decode_chunks' that decode at 64 ... 1024 keys per partial")
     ap.add_argument("--ab", nargs=2, metavar=("LIB_A", "LIB_B"),
                     help="paired A/B of two builds of libattn.so on --part")
     ap.add_argument("--part", default="headline", help="workload of --ab")

@@ -87,6 +87,18 @@ def cmd_trace(a):
         lines.append(f"| `{_short(n)}` | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     sel = _pick(tr, a.kernel, "traced")
+    seg_note = ""
+    if a.segment is not None:
+        # runs of dispatches separated by more than gap_ms of idle time
+        segs = [[sel[0]]]
+        for prev, cur in zip(sel, sel[1:]):
+            if cur[1] - prev[2] > a.gap_ms * 1e6:
+                segs.append([])
+            segs[-1].append(cur)
+        seg_note = (f" Split at idle gaps over {a.gap_ms} ms the dispatches form runs of "
+                    f"{', '.join(str(len(x)) for x in segs)}; run {a.segment} is kept"
+                    + (f", its last {a.tail}" if a.tail else "") + ".")
+        sel = segs[a.segment][-a.tail:] if a.tail else segs[a.segment]
     durs = [(e - s) / 1e3 for _, s, e in sel]
     timed = durs[a.skip:a.skip + a.first] if a.first else durs[a.skip:]
     if not timed:
@@ -94,7 +106,7 @@ def cmd_trace(a):
     mean, med = statistics.mean(timed), statistics.median(timed)
     lines += ["", f"Kernel `{_short(sel[0][0])}`: {len(durs)} dispatches; the first {a.skip} "
                   f"(warm-up) are dropped" + (f", the {len(timed)} after them are the timed "
-                                              f"launches" if a.first else "") + ".", ""]
+                                              f"launches" if a.first else "") + "." + seg_note, ""]
     if len(durs) <= 64:
         lines += ["Per-dispatch durations (us): " + ", ".join(f"{x:.1f}" for x in durs) + ".", ""]
     lines += ["| timed launches | value |", "|---|---|",
@@ -262,6 +274,9 @@ def main():
     t.add_argument("--flops", type=float)
     t.add_argument("--bytes", type=float)
     t.add_argument("--bench")
+    t.add_argument("--segment", type=int, help="keep one run of dispatches (split at idle gaps)")
+    t.add_argument("--tail", type=int, default=0, help="of that run, keep the last N")
+    t.add_argument("--gap-ms", type=float, default=1.0)
     c = sub.add_parser("counters")
     c.add_argument("--dir", nargs="+", required=True)
     c.add_argument("--trace")
