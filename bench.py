@@ -295,7 +295,10 @@ def load_probe():
         lib.attn_probe_mfma.argtypes = [i, i, i, vp, vp]
         lib.attn_probe_read.argtypes = [vp, sz, i, vp, vp]
         lib.attn_probe_empty.argtypes = [i, vp]
-        for f in (lib.attn_probe_mfma, lib.attn_probe_read, lib.attn_probe_empty):
+        lib.attn_probe_valu.argtypes = [i, i, i, vp, vp]
+        lib.attn_probe_mix.argtypes = [i, i, i, vp, vp]
+        for f in (lib.attn_probe_mfma, lib.attn_probe_read, lib.attn_probe_empty,
+                  lib.attn_probe_valu, lib.attn_probe_mix):
             f.restype = i
         _PROBE = lib
     return _PROBE
@@ -329,6 +332,45 @@ def measured_peaks():
     del x, y
     log(f"measured peaks: {res}")
     return res
+
+
+VALU_KINDS = ("v_exp_f32", "v_fma_f32", "v_cvt_pk_bf16_f32", "v_cvt_pk_fp8_f32", "v_max3_f32",
+              "v_dot2c_f32_bf16")
+
+
+def valu_costs():
+    """Issue cost of the softmax's vector instructions (attn_probe_valu, 8
+    waves per SIMD: ns per wave instruction per SIMD, and relative to the FMA),
+    and the bf16 MFMA rate with vector work beside it (attn_probe_mix, 2 waves
+    per SIMD: percent of the MFMA-only rate per vector instructions per MFMA)."""
+    import torch
+    probe = load_probe()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(8 * cus * 256, dtype=torch.float32, device="cuda:0")
+    iters = 2000
+    ns = {}
+    for kind, name in enumerate(VALU_KINDS):
+        blocks = 8 * cus
+        ms = time_events(lambda: _probe_call(probe.attn_probe_valu(kind, iters, blocks, out.data_ptr(),
+                                                                   stream), "attn_probe_valu"), 3, 1)
+        ns[name] = ms * 1e6 / (8 * iters * 16)
+    costs = {k: {"ns_per_wave_instruction_per_simd": round(v, 3),
+                 "relative_to_fma": round(v / ns["v_fma_f32"], 2)} for k, v in ns.items()}
+    mix = {}
+    base = None
+    for nv in (0, 4, 8, 12, 16, 24, 32):
+        blocks = 2 * cus
+        ms = time_events(lambda: _probe_call(probe.attn_probe_mix(nv, iters, blocks, out.data_ptr(),
+                                                                  stream), "attn_probe_mix"), 3, 1)
+        per = ms * 1e6 / (2 * iters * 4)   # ns per MFMA per SIMD
+        base = per if nv == 0 else base
+        mix[str(nv / 4)] = {"ns_per_mfma_per_simd": round(per, 3),
+                            "mfma_rate_pct": round(100 * base / per, 1)}
+    log(f"vector instruction costs: {costs}")
+    log(f"MFMA rate beside vector work (vector instructions per MFMA -> % of MFMA-only): "
+        f"{ {k: v['mfma_rate_pct'] for k, v in mix.items()} }")
+    return {"valu_costs": costs, "mfma_beside_valu": mix}
 
 
 def graph_us_per_call(calls, reps=20):
@@ -531,6 +573,8 @@ def run_extra(part):
                               "gbs_cold": round(nbytes / (cold_us * 1e-6) / 1e9, 1)}
             log(f"decode sweep Nk={nk}: {cold_us:.2f} us, {sweep[str(nk)]['gbs_cold']} GB/s")
         extra["decode_kv_sweep"] = sweep
+    elif part == "valu":
+        extra.update(valu_costs())
     elif part == "decode_chunks":
         extra["decode_chunks"] = decode_chunk_sweep()
     elif part in ("decode_cold", "decode_kvq_cold"):
@@ -672,7 +716,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
     ap.add_argument("--only", choices=["decode", "decode_kvq", "decode_cold", "decode_kvq_cold",
-                                       "decode_chunks",
+                                       "decode_chunks", "valu",
                                        "quant", "mx", "rope", "causal", "sliding", "sdxl", "copy",
                                        "floor"],
                     help="time one secondary workload only (for kernel profiles); "
@@ -680,7 +724,8 @@ def main():
                          "scaling the FETCH_SIZE / WRITE_SIZE counters; 'floor' the "
                          "empty-launch and bare-read floors under the decode; "
                          "'decode_cold' / 'decode_kvq_cold' the cold Nk = 4096 decode alone; "
-                         "'decode_chunks' that decode at 64 ... 1024 keys per partial")
+                         "'decode_chunks' that decode at 64 ... 1024 keys per partial; "
+                         "'valu' the vector-instruction and MFMA-beside-vector probes")
     ap.add_argument("--ab", nargs=2, metavar=("LIB_A", "LIB_B"),
                     help="paired A/B of two builds of libattn.so on --part")
     ap.add_argument("--part", default="headline", help="workload of --ab")

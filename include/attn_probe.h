@@ -43,6 +43,25 @@ int attn_probe_read(const void* x, size_t nbytes, int blocks, uint32_t* out, voi
  * of one kernel. Invalid: blocks outside 1..65535. */
 int attn_probe_empty(int blocks, void* stream);
 
+/* Issue cost of one kind of vector instruction: `blocks` workgroups of 4
+ * waves, each wave `iters` x 16 instructions on 16 independent chains.
+ *   kind 0: v_exp_f32   1: v_fma_f32   2: v_cvt_pk_bf16_f32
+ *   kind 3: v_cvt_pk_fp8_f32   4: v_max3_f32   5: v_dot2c_f32_bf16
+ *   out: blocks * 256 floats (4-byte aligned), written with the chain values
+ *        so the work cannot be dropped.
+ * Invalid: out NULL or misaligned, kind outside 0..5, iters < 1, blocks
+ * outside 1..65535. */
+int attn_probe_valu(int kind, int iters, int blocks, float* out, void* stream);
+
+/* The bf16 MFMA rate beside vector work: per wave `iters` rounds of 4
+ * v_mfma_f32_32x32x16_bf16 on four independent accumulators, each followed by
+ * nv / 4 vector instructions (v_exp_f32 and v_fma_f32 in the ratio 1 : 2) on
+ * registers the MFMAs do not use. nv in {0, 4, 8, 12, 16, 24, 32}.
+ *   out: blocks * 256 floats (4-byte aligned).
+ * Invalid: out NULL or misaligned, another nv, iters < 1, blocks outside
+ * 1..65535. */
+int attn_probe_mix(int nv, int iters, int blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

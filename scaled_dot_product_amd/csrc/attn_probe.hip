@@ -9,6 +9,12 @@
 //                     four loads in flight per lane), the floor of a
 //                     bandwidth-bound kernel of that size
 //   attn_probe_empty  a launch that does nothing, the floor of any kernel
+//   attn_probe_valu   the issue cost of one kind of vector instruction (16
+//                     independent chains per wave), for the softmax's
+//                     instruction mix: exponential, FMA, bf16 and fp8 packing,
+//                     three-way maximum, bf16 pair dot product
+//   attn_probe_mix    the bf16 MFMA rate with nv vector instructions (one
+//                     exponential to two FMAs) issued beside every 4 MFMAs
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -104,6 +110,73 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const u32x4* __restrict
 
 __global__ void probe_empty_kernel() {}
 
+// Vector-instruction issue cost: iters rounds of 16 independent instructions
+// of one kind per wave (each register its own dependency chain).
+template <int KIND>
+__global__ void __launch_bounds__(256) probe_valu_kernel(float* out, int iters) {
+  float r[16], s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    r[i] = 0.37f * (i + 1) + 1e-3f * threadIdx.x;
+    s[i] = 0.5f * r[i];
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (KIND == 0) asm volatile("v_exp_f32 %0, %0" : "+v"(r[i]));
+      if constexpr (KIND == 1) asm volatile("v_fma_f32 %0, %0, %1, %1" : "+v"(r[i]) : "v"(s[i]));
+      if constexpr (KIND == 2) asm volatile("v_cvt_pk_bf16_f32 %0, %0, %1" : "+v"(r[i]) : "v"(s[i]));
+      if constexpr (KIND == 3) asm volatile("v_cvt_pk_fp8_f32 %0, %1, %1" : "+v"(r[i]) : "v"(s[i]));
+      if constexpr (KIND == 4) asm volatile("v_max3_f32 %0, %0, %1, %1" : "+v"(r[i]) : "v"(s[i]));
+      if constexpr (KIND == 5) asm volatile("v_dot2c_f32_bf16 %0, %1, %1" : "+v"(r[i]) : "v"(s[i]));
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += r[i];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+// bf16 32x32x16 MFMAs on four independent accumulators, each group of four
+// followed by NV vector instructions (an exponential, then two FMAs, repeating,
+// on 16 chains that the MFMAs do not touch).
+template <int NV>
+__global__ void __launch_bounds__(256) probe_mix_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (lane + i));
+    b[i] = (__bf16)(0.002f * (i - lane));
+  }
+  float r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = 0.37f * (i + 1) + 1e-3f * threadIdx.x;
+  f32x16 c[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NV / 4; ++v) {
+        const int i = (NV / 4 * k + v) & 15;
+        if ((NV / 4 * k + v) % 3 == 0)
+          asm volatile("v_exp_f32 %0, %0" : "+v"(r[i]));
+        else
+          asm volatile("v_fma_f32 %0, %0, %0, %0" : "+v"(r[i]));
+      }
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += c[k][j];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += r[i];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 }  // namespace attn
@@ -130,6 +203,39 @@ int attn_probe_read(const void* x, size_t nbytes, int blocks, uint32_t* out, voi
     return -1;
   hipLaunchKernelGGL(attn::probe_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      (const attn::u32x4*)x, (int64_t)(nbytes / 16), out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int attn_probe_valu(int kind, int iters, int blocks, float* out, void* stream) {
+  if (out == nullptr || ((uintptr_t)out & 3u) || kind < 0 || kind > 5 || iters < 1 || blocks < 1 ||
+      blocks > 65535)
+    return -1;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((attn::probe_valu_kernel<0>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 1: hipLaunchKernelGGL((attn::probe_valu_kernel<1>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 2: hipLaunchKernelGGL((attn::probe_valu_kernel<2>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 3: hipLaunchKernelGGL((attn::probe_valu_kernel<3>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 4: hipLaunchKernelGGL((attn::probe_valu_kernel<4>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    default: hipLaunchKernelGGL((attn::probe_valu_kernel<5>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int attn_probe_mix(int nv, int iters, int blocks, float* out, void* stream) {
+  if (out == nullptr || ((uintptr_t)out & 3u) || iters < 1 || blocks < 1 || blocks > 65535)
+    return -1;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (nv) {
+    case 0: hipLaunchKernelGGL((attn::probe_mix_kernel<0>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 4: hipLaunchKernelGGL((attn::probe_mix_kernel<4>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 8: hipLaunchKernelGGL((attn::probe_mix_kernel<8>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 12: hipLaunchKernelGGL((attn::probe_mix_kernel<12>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 16: hipLaunchKernelGGL((attn::probe_mix_kernel<16>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 24: hipLaunchKernelGGL((attn::probe_mix_kernel<24>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    case 32: hipLaunchKernelGGL((attn::probe_mix_kernel<32>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    default: return -1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

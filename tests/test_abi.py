@@ -39,6 +39,8 @@ def probe(lib):
     p.attn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.c_void_p]
     p.attn_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    p.attn_probe_valu.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    p.attn_probe_mix.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
     return p
 
 
@@ -53,7 +55,8 @@ def test_header_declares_the_boundary():
         assert n in names
     assert "attn_probe_mfma" not in names     # measurement probes live in their own library
     assert _declared_functions(PROBE_HEADER) == ["attn_probe_empty", "attn_probe_mfma",
-                                                 "attn_probe_read"]
+                                                 "attn_probe_mix", "attn_probe_read",
+                                                 "attn_probe_valu"]
 
 
 def test_library_exports_every_declared_symbol(lib, probe):
@@ -240,6 +243,18 @@ def test_probe_rejects_before_enqueue(probe):
     assert r(FAKE, 1024, 0, FAKE, None) == E_INVALID
     assert probe.attn_probe_empty(0, None) == E_INVALID
     assert probe.attn_probe_empty(70000, None) == E_INVALID
+    v = probe.attn_probe_valu
+    assert v(0, 4, 2, None, None) == E_INVALID          # no output buffer
+    assert v(0, 4, 2, FAKE + 2, None) == E_INVALID      # misaligned
+    assert v(6, 4, 2, FAKE, None) == E_INVALID          # unknown kind
+    assert v(-1, 4, 2, FAKE, None) == E_INVALID
+    assert v(1, 0, 2, FAKE, None) == E_INVALID          # no iterations
+    assert v(1, 4, 65536, FAKE, None) == E_INVALID      # grid too large
+    m = probe.attn_probe_mix
+    assert m(0, 4, 2, None, None) == E_INVALID
+    assert m(5, 4, 2, FAKE, None) == E_INVALID          # not a built vector count
+    assert m(8, 0, 2, FAKE, None) == E_INVALID
+    assert m(8, 4, 0, FAKE, None) == E_INVALID
 
 
 def test_mx_entry_points_reject_before_enqueue(lib):

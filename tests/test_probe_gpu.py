@@ -37,3 +37,25 @@ def test_probe_read_and_empty_run():
     for v in out.cpu().tolist():
         folded ^= v & 0xFFFFFFFF
     assert folded == 0x04030201
+
+
+@pytest.mark.parametrize("kind", range(6))
+def test_probe_valu_runs(kind):
+    blocks = 8
+    out = torch.full((blocks * 256,), 0x7FBADBAD, dtype=torch.int32, device="cuda:0")
+    st = bench.load_probe().attn_probe_valu(kind, 4, blocks, out.data_ptr(),
+                                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert (out != 0x7FBADBAD).all()     # every thread wrote its chain sum
+
+
+@pytest.mark.parametrize("nv", [0, 4, 8, 12, 16, 24, 32])
+def test_probe_mix_runs(nv):
+    blocks = 8
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = bench.load_probe().attn_probe_mix(nv, 4, blocks, out.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert (out.view(torch.int32) != torch.tensor(float("nan")).view(torch.int32).item()).all()
