@@ -92,7 +92,15 @@ typedef enum {
  *   dtype        attn_dtype of q, k, v and o.
  *   workspace    device scratch of at least attn_fwd_workspace_bytes(...)
  *                bytes (may be NULL when that is 0); contents need no
- *                initialisation and are clobbered.
+ *                initialisation and are clobbered. 256-byte aligned.
+ *                In the exact mode, a prefill whose grid fills the GPU
+ *                less than once (e.g. 2 x 10 heads x 4096 rows at head dim
+ *                64) splits each query tile's key range over 2-4
+ *                workgroups and merges their partials; the workspace holds
+ *                the partials. Given less than attn_fwd_workspace_bytes
+ *                but at least what the unsplit schedule needs (0 for
+ *                bf16/f16 inputs), the call runs unsplit: the same result
+ *                up to rounding.
  *   stream       hipStream_t to enqueue on.
  *
  * A row with no visible key (window_lo > pos0 + i) is written as exact zeros.
@@ -105,8 +113,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
 
 /*
  * attn_fwd_workspace_bytes — workspace attn_fwd needs for these arguments
- * (same meaning as above). Host-only; never touches the GPU. Returns 0 for
- * arguments attn_fwd would reject.
+ * (same meaning as above), the split prefill's partials included.
+ * Host-only; never touches the GPU. Returns 0 for arguments attn_fwd would
+ * reject.
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                 int causal, int window_lo, int pos0,
@@ -340,7 +349,10 @@ typedef struct {
   int waves;               /* waves of 64 lanes per workgroup */
   int rows;                /* prefill: query rows per workgroup; decode: packed
                               query rows per key/value head (G * Nq) */
-  int splits;              /* decode: workgroups per key/value head; else 1 */
+  int splits;              /* decode: workgroups per key/value head; exact
+                              prefill: workgroups per query tile (1, or 2-4
+                              for grids that fill the GPU less than once,
+                              given the full workspace); else 1 */
   long long workgroups;    /* workgroups of the attention launch */
   int pre_launches;        /* launches enqueued before it (fp32 -> bf16
                               conversions, quantisers, the K rotation pass) */
@@ -362,15 +374,16 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int
  * Arguments, layouts, modes and results are those of attn_fwd (the same
  * kernels run); the caller passes only inputs and outputs. Errors:
  *   every attn_fwd argument error, checked first (nothing enqueued);
- *   ATTN_E_TOO_LARGE  attn_fwd_workspace_bytes(...) > ATTN_NOALLOC_SCRATCH_BYTES
- *                     (e.g. the quantised modes at long sequences, fp32 inputs
- *                     beyond about 2 M elements);
+ *   ATTN_E_TOO_LARGE  the call needs more workspace than ATTN_NOALLOC_SCRATCH_BYTES
+ *                     even unsplit (e.g. the quantised modes at long sequences,
+ *                     fp32 inputs beyond about 2 M elements); a split prefill
+ *                     whose partials do not fit runs unsplit instead;
  *   ATTN_E_INVALID    `stream` belongs to another device than the current one;
  *   ATTN_E_HIP        the device address could not be looked up, or a launch
  *                     failed.
  * Calls on one GPU share its array, which keeps the last call's contents (no
- * kernel here needs it cleared: the decode's arrival counters carry a per-call
- * tag), so calls that overlap on one GPU (different streams, or concurrent host
+ * kernel here needs it cleared: the arrival counters of the decode and of the
+ * split prefill carry a per-call tag), so calls that overlap on one GPU (different streams, or concurrent host
  * threads) race and must be serialised by the caller.
  */
 #define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)

@@ -216,6 +216,13 @@ static void* attn_worker(void* arg) {
 }
 
 static int run_attn(attn_job* J, int nthreads) {
+  /* a row list must name rows that exist */
+  if (J->nrows < 0) return -1;
+  if (J->rows) {
+    const int64_t total = (int64_t)J->B * J->Hq * J->Nq;
+    for (int64_t s = 0; s < J->nrows; ++s)
+      if (J->rows[s] < 0 || J->rows[s] >= total) return -1;
+  }
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   pthread_t th[256];

@@ -84,14 +84,18 @@ struct Layout {
   size_t qc = 0, qs = 0, kc = 0, ks = 0, vc = 0, vs = 0;  // quantised mode
   size_t dec = 0;                                  // decode partials
   size_t rk = 0;                                   // rotated K (exact mode with RoPE)
+  size_t spl = 0;                                  // split-prefill counters and partials
   size_t total = 0;
   bool decode = false;
   DecodePlan plan{};
+  PrefillSplit split{};
 };
 
 // force_decode >= 0: the decode kernel with that split request (0 = the
 // library's own plan), whatever the key count; -1: attn_fwd's dispatch.
-Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1) {
+// allow_split: the exact prefill may split small grids (needs workspace).
+Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1,
+                   bool allow_split = true) {
   Layout L;
   size_t off = 0;
   const size_t nq = (size_t)a.B * a.Hq * a.Nq * a.D;
@@ -129,6 +133,11 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1)
     L.decode = true;
     L.plan = decode_plan(a, force_decode > 0 ? force_decode : 0);
     L.dec = off; off = round_up(off + L.plan.ws_bytes);
+  } else if (allow_split) {
+    L.split = prefill_split_plan(a, dtype == ATTN_DT_F32 ? 4 : 2);
+    if (L.split.ns > 1) {
+      L.spl = off; off = round_up(off + L.split.ws_bytes);
+    }
   }
   L.total = off;
   return L;
@@ -186,7 +195,9 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
                  void* stream, int force_decode = -1) {
   const int B = a.B, Hq = a.Hq, Hkv = a.Hkv, Nq = a.Nq, Nk = a.Nk, D = a.D;
   const void *q = a.q, *k = a.k, *v = a.v;
-  const Layout L = plan_layout(a, mode, dtype, force_decode);
+  Layout L = plan_layout(a, mode, dtype, force_decode);
+  // A workspace too small for the split prefill runs it unsplit.
+  if (L.split.ns > 1 && workspace_bytes < L.total) L = plan_layout(a, mode, dtype, force_decode, false);
   if (L.total > 0) {
     if (workspace_bytes < L.total) return ATTN_E_WORKSPACE;
     if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) != 0) return ATTN_E_INVALID;
@@ -251,11 +262,20 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   if (L.decode)
     e = launch_decode(a, L.plan, elem, out_f32, ws + L.dec, s);
   else
-    e = launch_prefill(a, elem, out_f32, s);
+    e = launch_prefill(a, elem, out_f32, L.split, L.split.ns > 1 ? ws + L.spl : nullptr, s);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 }  // namespace
+
+size_t fwd_min_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                               int window_lo, int pos0, int mode, int dtype) {
+  if (check_fwd(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, 1.0f, mode, dtype) != ATTN_OK)
+    return 0;
+  FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, D, causal,
+                        window_lo, pos0, 1.0f);
+  return plan_layout(a, mode, dtype, -1, false).total;
+}
 
 int fwd_validate(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
                  int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
@@ -474,7 +494,8 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int
     p.kernel = ATTN_KERNEL_PREFILL;
     p.waves = prefill_waves(a);
     p.rows = 32 * p.waves;
-    p.workgroups = (long long)B * Hq * ((Nq + p.rows - 1) / p.rows);
+    p.splits = L.split.ns;
+    p.workgroups = (long long)B * Hq * ((Nq + p.rows - 1) / p.rows) * L.split.ns;
     p.pre_launches = (dtype == ATTN_DT_F32 ? 3 : 0) + (rope ? 1 : 0);
   }
   *plan = p;

@@ -87,6 +87,25 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Arrival counting for a fused merge of partials (split-KV decode, split
+// prefill). A counter is (generation << 24) | arrivals. One thread of each
+// workgroup claims it for this call in two parts kept off the critical path:
+// it reads the counter behind its tile loads, and after its tiles, if the tag
+// read is not this call's generation (left by an earlier call, or
+// uninitialised workspace), it swaps the value read for (generation << 24). A
+// failed swap means another workgroup already claimed it. Arrival is then a
+// single agent-scope acquire-release add (after the workgroup's partial
+// stores have been acknowledged and its waves have met at a barrier); the
+// workgroup that sees nsplit - 1 earlier arrivals is last. It resets the
+// counter to 0, a tag no call uses, so replays of a captured graph (same
+// generation) claim it again. Every swap precedes its own workgroup's
+// arrival, so all of them precede the reset.
+__device__ __forceinline__ bool arrive_last(unsigned long long* c, int nsplit) {
+  const unsigned long long old =
+      __hip_atomic_fetch_add(c, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  return (int)(old & 0xffffffull) == nsplit - 1;
+}
+
 // gfx950 LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group,
 // lane 4a + e receives element e of the four 8-byte rows whose addresses
 // lanes a, a+4, a+8 and a+12 supply. The body exists only in the device pass

@@ -97,23 +97,6 @@ __device__ __forceinline__ float get1(const float* src) {
   return __uint_as_float(__hip_atomic_load((unsigned*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Arrival counting for the fused merge. The counter of a key/value head is
-// (generation << 24) | arrivals. One thread of each workgroup claims it for
-// this call in two parts kept off the critical path: it reads the counter
-// behind its tile loads, and after its tiles, if the tag read is not this
-// call's generation (left by an earlier call, or uninitialised workspace), it
-// swaps the value read for (generation << 24). A failed swap means another
-// workgroup already claimed it. Arrival is then a single atomic add; the
-// workgroup that sees nsplit - 1 earlier arrivals is last. It resets the
-// counter to 0, a tag no call uses, so replays of a captured graph (same
-// generation) claim it again. Every swap precedes its own workgroup's
-// arrival, so all of them precede the reset.
-__device__ bool arrive_last(unsigned long long* c, int nsplit) {
-  const unsigned long long old =
-      __hip_atomic_fetch_add(c, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  return (int)(old & 0xffffffull) == nsplit - 1;
-}
-
 // After the tiles: the counter claim, the merge of the waves' partials in LDS
 // (so: kWaves x 32 x D floats, sml: 2 x kWaves x 32 floats), the workgroup's
 // partial published, the arrival, and in the last workgroup of the KV head
@@ -840,16 +823,6 @@ decode_kvq_kernel(FwdArgs a, DecodeArgs p, const int8_t* __restrict__ kc,
   decode_finish<TO, D, kWaves>(a, p, m, l, oacc, (float*)lds, sml, ctr_seen);
 }
 
-// A different generation for every launch, from a per-process random start
-// (so that counters left in a reused workspace by another process never match).
-unsigned long long next_generation() {
-  static std::atomic<unsigned long long> counter{
-      ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
-       (unsigned long long)(uintptr_t)&counter) * 0x9E3779B97F4A7C15ull};
-  const unsigned long long g = counter.fetch_add(1, std::memory_order_relaxed);
-  return (g % ((1ull << 40) - 1)) + 1;
-}
-
 DecodeArgs decode_args(const FwdArgs& a, const DecodePlan& pl, void* ws) {
   DecodeArgs p;
   p.rows = pl.rows;
@@ -891,6 +864,16 @@ hipError_t launch_kvq_t(const FwdArgs& a, const DecodePlan& pl, const int8_t* kc
 }
 
 }  // namespace
+
+// A different generation for every launch, from a per-process random start
+// (so that counters left in a reused workspace by another process never match).
+unsigned long long next_generation() {
+  static std::atomic<unsigned long long> counter{
+      ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+       (unsigned long long)(uintptr_t)&counter) * 0x9E3779B97F4A7C15ull};
+  const unsigned long long g = counter.fetch_add(1, std::memory_order_relaxed);
+  return (g % ((1ull << 40) - 1)) + 1;
+}
 
 bool decode_supported(const FwdArgs& a) {
   return (int64_t)(a.Hq / a.Hkv) * a.Nq <= 32 && (int64_t)a.B * a.Hkv <= 65535;

@@ -39,6 +39,10 @@ struct FwdArgs {
 int fwd_validate(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
                  int Nq, int Nk, int D, int causal, int window_lo, int pos0, float scale, int mode,
                  int dtype);
+// The least workspace attn_fwd accepts for these sizes (the split prefill
+// off); attn_fwd_workspace_bytes gives the size that enables it.
+size_t fwd_min_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal,
+                               int window_lo, int pos0, int mode, int dtype);
 
 // Visible key range [lo, hi) over all rows of a call (hi <= lo: none).
 struct KeyRange {
@@ -47,10 +51,28 @@ struct KeyRange {
 KeyRange key_range(const FwdArgs& a);
 
 // ---- exact-mode prefill (bf16/f16 MFMA) ----------------------------------
-// elem: 1 = f16, 2 = bf16 operands; out_f32: write fp32 output.
-hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s);
+// Split of each query tile's key range over ns workgroups (ns = 1: none). A
+// grid of few query tiles leaves most CUs idle; ns parts of about equal
+// length per tile put them to work. Each part publishes its normalised
+// partial (O / l in the output type, m and l in fp32) and the last part of a
+// query tile to arrive merges them.
+struct PrefillSplit {
+  int ns = 1;              // parts per query tile
+  int64_t tiles = 0;       // query tiles (the unsplit grid)
+  int rows = 0;            // query rows per tile
+  size_t ctr_bytes = 0;    // arrival counters, one per query tile
+  size_t ws_bytes = 0;     // counters + partials
+};
+// out_bytes: bytes per output element (2, or 4 for fp32 output).
+PrefillSplit prefill_split_plan(const FwdArgs& a, int out_bytes);
+// elem: 1 = f16, 2 = bf16 operands; out_f32: write fp32 output. ws: the
+// split's workspace (ws_bytes of sp), unused when sp.ns == 1.
+hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, const PrefillSplit& sp,
+                          void* ws, hipStream_t s);
 // Waves (of 32 query rows each) per prefill workgroup for this call: 4 or 8.
 int prefill_waves(const FwdArgs& a);
+// A different value for every launch (tags of the arrival counters).
+unsigned long long next_generation();
 
 // ---- split-KV decode + log-sum-exp merge ---------------------------------
 struct DecodePlan {

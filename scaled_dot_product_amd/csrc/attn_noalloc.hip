@@ -53,8 +53,9 @@ extern "C" int attn_fwd_noalloc(const void* q, const void* k, const void* v, voi
   int st = attn::fwd_validate(q, k, v, o, B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0, scale,
                               mode, dtype);
   if (st != ATTN_OK) return st;
-  const size_t need = attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal, window_lo, pos0,
-                                               mode, dtype);
+  // (the split prefill runs only where its workspace fits in the array too)
+  const size_t need = attn::fwd_min_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, causal, window_lo,
+                                                    pos0, mode, dtype);
   if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_TOO_LARGE;
   if (stream != nullptr) {
     int sdev = -1, cur = -1;

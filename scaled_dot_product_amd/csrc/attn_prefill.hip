@@ -61,13 +61,121 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int kKPre = PREFILL_KPRE;
 constexpr int kVPre = PREFILL_VPRE;
 
+// The split of the query tiles' key ranges (one launch; ns = 1: no split).
+struct SplitArgs {
+  int ns;                    // parts per query tile
+  unsigned long long* ctr;   // [tiles] arrivals: (generation << 24) | count
+  unsigned long long gen;    // in [1, 2^40), different for every launch
+  void* opart;               // [tiles][ns][rows][D] of O_s / l_s in the output type
+  float* mlpart;             // [tiles][ns][rows][2]: m_s (exp2 units), l_s
+};
+
+// Store 4 consecutive channels of one row in the output element type.
+template <typename TO>
+__device__ __forceinline__ void put4(TO* p, const float (&v)[4]) {
+  if constexpr (sizeof(TO) == 4) {
+    *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    TO o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(v[r]);
+    *(u32x2*)p = *(const u32x2*)o4;
+  }
+}
+template <typename TO>
+__device__ __forceinline__ void get4(const TO* p, float (&v)[4]) {
+  if constexpr (sizeof(TO) == 4) {
+    const f32x4 x = *(const f32x4*)p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = x[r];
+  } else {
+    const u32x2 x = *(const u32x2*)p;
+    const TO* e = (const TO*)&x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (float)e[r];
+  }
+}
+
+// The end of one part of a split query tile: publish the normalised partial
+// (O / l in the output type, m and l in fp32), arrive, and in the tile's
+// last part to arrive merge the ns partials with log-sum-exp weights
+// 2^(m_s - M) l_s and write O. Lane (col, half) holds channels
+// 32 db + 8 a4 + 4 half + (0..3) of row qrow, as in the plain epilogue.
+template <typename TO, int D, int BM>
+__device__ __forceinline__ void split_finish(const FwdArgs& a, const SplitArgs& sp,
+                                             unsigned long long ctr_seen, int tile, int part,
+                                             int q0, int qrow, float l, float inv, float m_run,
+                                             const f32x16 (&oacc)[D / 32]) {
+  constexpr int DB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  if (tid == 0 && (ctr_seen >> 24) != sp.gen) atomicCAS(sp.ctr + tile, ctr_seen, sp.gen << 24);
+  TO* op = (TO*)sp.opart;
+  const int64_t slot0 = (int64_t)tile * sp.ns * BM + (qrow - q0);   // this row, part 0
+  if (qrow < a.Nq) {
+    const int64_t r = slot0 + (int64_t)part * BM;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = oacc[db][4 * a4 + q] * inv;
+        put4<TO>(op + r * D + 32 * db + 8 * a4 + 4 * half, v);
+      }
+    if (half == 0) {
+      sp.mlpart[2 * r] = m_run;
+      sp.mlpart[2 * r + 1] = l;
+    }
+  }
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);   // every partial store of this thread acknowledged
+  __syncthreads();
+  if (tid == 0) s_last = arrive_last(sp.ctr + tile, sp.ns);
+  __syncthreads();
+  if (!s_last) return;
+  if (qrow < a.Nq) {
+    float M = -INFINITY;
+    for (int s = 0; s < sp.ns; ++s) M = fmaxf(M, sp.mlpart[2 * (slot0 + (int64_t)s * BM)]);
+    float L = 0.0f;
+    float acc[DB][4][4] = {};
+    for (int s = 0; s < sp.ns; ++s) {
+      const int64_t r = slot0 + (int64_t)s * BM;
+      const float ms = sp.mlpart[2 * r], ls = sp.mlpart[2 * r + 1];
+      // a part with no visible key has m = -inf and weight 0
+      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M) * ls;
+      L += w;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          float v[4];
+          get4<TO>(op + r * D + 32 * db + 8 * a4 + 4 * half, v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[db][a4][q] = fmaf(w, v[q], acc[db][a4][q]);
+        }
+    }
+    const float invL = L > 0.0f ? 1.0f / L : 0.0f;
+    TO* orow = (TO*)a.o + ((int64_t)(tile / ((a.Nq + BM - 1) / BM)) * a.Nq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[db][a4][q] * invL;
+        put4<TO>(orow + 32 * db + 8 * a4 + 4 * half, v);
+      }
+  }
+  if (tid == 0) __hip_atomic_store(sp.ctr + tile, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Head dim 128 runs 2 waves per SIMD; head dim 64 fits 3 (168 VGPRs, a few
 // spills outside the loop), which measured 1-3 % faster on the SDXL shape
 // and on long sequences.
 template <typename T, typename TO, int D, int W>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
                                amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
-prefill_kernel(FwdArgs a, int ntq) {
+prefill_kernel(FwdArgs a, int ntq, SplitArgs sp) {
   using E = Elem<T>;
   using V8 = typename E::vec8;
   constexpr int BM = 32 * W;       // W waves of 32 query rows
@@ -81,7 +189,10 @@ prefill_kernel(FwdArgs a, int ntq) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, col = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  // Workgroup -> (query tile, part of its key range); the parts of a tile
+  // are consecutive, so they run on one XCD.
+  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = job / sp.ns, part = job - tile * sp.ns;
   const int bh = tile / ntq, qt_in = tile - bh * ntq;
   // Causal rows see more keys the later they sit: a head's heaviest q-tiles
   // are dispatched first, so the light ones fill the end of the grid.
@@ -100,8 +211,12 @@ prefill_kernel(FwdArgs a, int ntq) {
   // (a per-row window: row q0 has the lowest bound)
   const int kv_lo = a.window_w > 0 ? max(a.window_lo, a.pos0 + q0 - a.window_w + 1) : a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
-  const int t_lo = kv_lo / 64;
-  const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
+  const int t_lo0 = kv_lo / 64;
+  const int nt0 = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo0 : 0;
+  // this part's tiles: [t_lo, t_lo + nt), ns nearly equal parts (some may be empty)
+  const int chunk = (nt0 + sp.ns - 1) / sp.ns;
+  const int t_lo = t_lo0 + part * chunk;
+  const int nt = max(0, min(chunk, nt0 - part * chunk));
 
   // Q^T as B operands, held for the whole loop: column = query row,
   // lane half h of k-step ks holds d = 16 ks + 8 h + (0..7).
@@ -118,6 +233,10 @@ prefill_kernel(FwdArgs a, int ntq) {
   // workgroup in registers (K arrives rotated)
   if (a.rope.on)
     rope_lane_row<T, KS>(qv, (float)(a.pos0 + qrow), half, a.rope.style, a.rope.rev_hi, a.rope.rev_lo);
+  // a split call: the tile's arrival counter, read now, claimed after the tiles
+  unsigned long long ctr_seen = 0;
+  if (sp.ns > 1 && tid == 0)
+    ctr_seen = __hip_atomic_load(sp.ctr + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // LDS tiles are 64 unpadded rows of D elements; chunk c of row r sits at
   // chunk position c ^ swz(r). K row r holds key (r & ~31) | swap23(r & 31)
@@ -404,6 +523,10 @@ prefill_kernel(FwdArgs a, int ntq) {
   // Epilogue: O = O_acc / l; rows with no visible key are written as zeros.
   const float l = halves_sum(l_run);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (sp.ns > 1) {
+    split_finish<TO, D, BM>(a, sp, ctr_seen, tile, part, q0, qrow, l, inv, m_run, oacc);
+    return;
+  }
   if (qrow < a.Nq) {
     TO* orow = Op + (int64_t)qrow * D;
 #pragma unroll
@@ -427,19 +550,31 @@ prefill_kernel(FwdArgs a, int ntq) {
 }
 
 template <typename T, typename TO, int D, int W>
-hipError_t launch_w(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_w(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStream_t s) {
   constexpr int BM = 32 * W;
   const int ntq = (a.Nq + BM - 1) / BM;
-  const int64_t grid = (int64_t)a.B * a.Hq * ntq;
+  const int64_t tiles = (int64_t)a.B * a.Hq * ntq;
+  SplitArgs sp{1, nullptr, 0, nullptr, nullptr};
+  if (pl.ns > 1) {
+    if (pl.tiles != tiles || pl.rows != BM || ws == nullptr) return hipErrorInvalidValue;
+    const int64_t nrow = tiles * pl.ns * BM;
+    sp.ns = pl.ns;
+    sp.ctr = (unsigned long long*)ws;
+    sp.opart = (char*)ws + pl.ctr_bytes;
+    sp.mlpart = (float*)((char*)ws + pl.ctr_bytes + ((size_t)nrow * D * sizeof(TO) + 255) / 256 * 256);
+    sp.gen = next_generation();
+  }
+  const int64_t grid = tiles * sp.ns;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, TO, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a, ntq);
+  hipLaunchKernelGGL((prefill_kernel<T, TO, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a, ntq,
+                     sp);
   return hipGetLastError();
 }
 
 template <typename T, typename TO, int D>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  if (prefill_waves(a) == 8) return launch_w<T, TO, D, 8>(a, s);
-  return launch_w<T, TO, D, 4>(a, s);
+hipError_t launch_t(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStream_t s) {
+  if (prefill_waves(a) == 8) return launch_w<T, TO, D, 8>(a, pl, ws, s);
+  return launch_w<T, TO, D, 4>(a, pl, ws, s);
 }
 
 }  // namespace
@@ -453,12 +588,45 @@ int prefill_waves(const FwdArgs& a) {
   return a.D == 128 && grid8 >= 8 * 256 ? 8 : 4;
 }
 
-hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, hipStream_t s) {
-  if (elem == 2) {
-    if (out_f32) return a.D == 64 ? launch_t<__bf16, float, 64>(a, s) : launch_t<__bf16, float, 128>(a, s);
-    return a.D == 64 ? launch_t<__bf16, __bf16, 64>(a, s) : launch_t<__bf16, __bf16, 128>(a, s);
+// Parts per query tile: grids of at most 128 query tiles are split into 2
+// to 4 parts of at least two key tiles each, as many as keep the split grid
+// within one workgroup per CU (256). Each part's publication and the merge
+// cost an agent-scope release and acquire, which write back and invalidate
+// the XCD's L2; with one workgroup per CU that is cheap (1.7-2.6 times
+// faster on 16-64 tiles), with several per CU the invalidations cost the
+// other workgroups their cached K/V tiles (a 640-tile grid split in two took
+// 30 % longer), so larger grids run unsplit.
+PrefillSplit prefill_split_plan(const FwdArgs& a, int out_bytes) {
+  PrefillSplit p;
+  const int W = prefill_waves(a);
+  p.rows = 32 * W;
+  p.tiles = (int64_t)a.B * a.Hq * ((a.Nq + p.rows - 1) / p.rows);
+  const KeyRange r = key_range(a);
+  const int nt = r.hi > r.lo ? (r.hi + 63) / 64 - r.lo / 64 : 0;
+  int ns = 1;
+  if (p.tiles * 2 <= 256) {
+    ns = (int)(256 / p.tiles);
+    ns = ns > 4 ? 4 : ns;
+    while (ns > 1 && nt < 2 * ns) --ns;
   }
-  return a.D == 64 ? launch_t<_Float16, _Float16, 64>(a, s) : launch_t<_Float16, _Float16, 128>(a, s);
+  p.ns = ns;
+  if (ns > 1) {
+    const size_t nrow = (size_t)p.tiles * ns * p.rows;
+    p.ctr_bytes = ((size_t)p.tiles * sizeof(unsigned long long) + 255) / 256 * 256;
+    p.ws_bytes = p.ctr_bytes + (nrow * a.D * out_bytes + 255) / 256 * 256 + nrow * 2 * sizeof(float);
+  }
+  return p;
+}
+
+hipError_t launch_prefill(const FwdArgs& a, int elem, bool out_f32, const PrefillSplit& sp,
+                          void* ws, hipStream_t s) {
+  if (elem == 2) {
+    if (out_f32)
+      return a.D == 64 ? launch_t<__bf16, float, 64>(a, sp, ws, s) : launch_t<__bf16, float, 128>(a, sp, ws, s);
+    return a.D == 64 ? launch_t<__bf16, __bf16, 64>(a, sp, ws, s) : launch_t<__bf16, __bf16, 128>(a, sp, ws, s);
+  }
+  return a.D == 64 ? launch_t<_Float16, _Float16, 64>(a, sp, ws, s)
+                   : launch_t<_Float16, _Float16, 128>(a, sp, ws, s);
 }
 
 // fp32 -> bf16, round to nearest even (the hardware conversion).

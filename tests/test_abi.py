@@ -361,7 +361,7 @@ def test_dispatch_of_the_five_workloads(lib):
     import torch
     want = {
         # name: (kernel, waves, rows, splits, workgroups, pre_launches)
-        "tiny_fp32_256": (sdpa.KERNEL_PREFILL, 4, 128, 1, 4, 3),
+        "tiny_fp32_256": (sdpa.KERNEL_PREFILL, 4, 128, 2, 8, 3),
         "gqa_decode_f16_4096": (sdpa.KERNEL_DECODE, 4, 8, 16, 128, 0),
         "sdxl_1024px_bf16": (sdpa.KERNEL_PREFILL, 4, 128, 1, 640, 0),
         "video_dit_bf16_32760": (sdpa.KERNEL_PREFILL, 8, 256, 1, 5120, 0),
@@ -380,6 +380,40 @@ def test_dispatch_of_the_five_workloads(lib):
     p = sdpa.plan(1, 16, 8, 4, 4096, 128, causal=True, window_lo=1000, pos0=4092,
                   dtype=torch.float16)
     assert p.kernel == sdpa.KERNEL_DECODE and p.splits == 13
+
+
+def test_prefill_split_policy(lib):
+    """Grids of at most 128 query tiles split each tile's key range into 2-4
+    parts of >= 2 key tiles, as many as keep the split grid within 256
+    workgroups; the workspace holds one counter per tile and a partial (O / l
+    in the output type, m and l in fp32) per part and row."""
+    import torch
+    # 64 tiles -> 4 parts; counters + 256 x 128 x (64 x 2 + 8) bytes
+    p = _plan(B=1, Hq=8, Hkv=8, Nq=1024, Nk=4096, D=64)
+    assert (p.splits, p.workgroups) == (4, 256)
+    assert p.workspace_bytes == 512 + 256 * 128 * 64 * 2 + 256 * 128 * 8
+    # 128 tiles -> 2 parts; 129 tiles -> none, no workspace
+    p = _plan(B=1, Hq=128, Hkv=1, Nq=128, Nk=4096, D=64)
+    assert (p.splits, p.workgroups) == (2, 256)
+    p = _plan(B=1, Hq=129, Hkv=1, Nq=128, Nk=4096, D=64)
+    assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 129, 0)
+    # SDXL (640 tiles) runs unsplit
+    p = _plan(B=2, Hq=10, Hkv=10, Nq=4096, Nk=4096, D=64)
+    assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 640, 0)
+    # 85 tiles -> 3 parts; head dim 128 the same
+    assert _plan(B=1, Hq=85, Hkv=1, Nq=128, Nk=4096, D=128).splits == 3
+    # parts keep >= 2 key tiles each
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=4096, D=64).splits == 4
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=384, D=64).splits == 3
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64).splits == 2
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=255, D=64).splits == 2    # 4 tiles, the last ragged
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=192, D=64).splits == 1
+    # fp32 output: 4-byte partials, after the three bf16 staging copies
+    p = _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, dtype=0)
+    staging = 3 * 2 * 256 * 64 * 2
+    assert p.workspace_bytes == staging + 256 + 8 * 128 * (64 * 4 + 8)
+    # the quantised mode never splits this way
+    assert _plan(B=1, Hq=8, Hkv=8, Nq=1024, Nk=4096, D=64, mode=sdpa.MODE_QUANT).splits == 1
 
 
 def test_dispatch_boundaries(lib):

@@ -254,6 +254,11 @@ def test_row_subset_equals_full():
     rows = np.array([0, 5, 32, 33, 100, 263], dtype=np.int64)
     sub = oracle.attn(q, k, v, scale=0.2, causal=True, pos0=20, rows=rows)
     np.testing.assert_array_equal(sub, full[rows])
+    # a row list may only name rows that exist (2 x 4 x 33 = 264 of them)
+    for bad in (264, -1):
+        with pytest.raises(ValueError):
+            oracle.attn(q, k, v, scale=0.2, causal=True, pos0=20,
+                        rows=np.array([0, bad], dtype=np.int64))
 
 
 def test_input_widening_is_exact_for_every_f16_and_bf16_code():
