@@ -94,10 +94,13 @@ typedef enum {
  *                bytes (may be NULL when that is 0); contents need no
  *                initialisation and are clobbered. 256-byte aligned.
  *                In the exact mode, a prefill whose grid fills the GPU
- *                less than once (e.g. 2 x 10 heads x 4096 rows at head dim
- *                64) splits each query tile's key range over 2-4
- *                workgroups and merges their partials; the workspace holds
- *                the partials. Given less than attn_fwd_workspace_bytes
+ *                less than once splits key ranges over several workgroups
+ *                and merges their partials (at most 128 query tiles: each
+ *                tile's keys over 2-4 workgroups; up to one round of
+ *                workgroups, e.g. 2 x 10 heads x 4096 rows at head dim 64:
+ *                enough tiles in two halves that every CU gets the same
+ *                work, merged by a second launch); the workspace holds the
+ *                partials. Given less than attn_fwd_workspace_bytes
  *                but at least what the unsplit schedule needs (0 for
  *                bf16/f16 inputs), the call runs unsplit: the same result
  *                up to rounding.
@@ -350,9 +353,12 @@ typedef struct {
   int rows;                /* prefill: query rows per workgroup; decode: packed
                               query rows per key/value head (G * Nq) */
   int splits;              /* decode: workgroups per key/value head; exact
-                              prefill: workgroups per query tile (1, or 2-4
-                              for grids that fill the GPU less than once,
-                              given the full workspace); else 1 */
+                              prefill: workgroups per query tile (1; 2-4 for
+                              grids of at most 128 query tiles; 2 for some
+                              tiles of a grid between half a round and one
+                              round of workgroups, which then takes a second,
+                              merging launch), given the full workspace;
+                              else 1 */
   long long workgroups;    /* workgroups of the attention launch */
   int pre_launches;        /* launches enqueued before it (fp32 -> bf16
                               conversions, quantisers, the K rotation pass) */

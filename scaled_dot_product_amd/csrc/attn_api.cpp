@@ -135,7 +135,7 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1,
     L.dec = off; off = round_up(off + L.plan.ws_bytes);
   } else if (allow_split) {
     L.split = prefill_split_plan(a, dtype == ATTN_DT_F32 ? 4 : 2);
-    if (L.split.ns > 1) {
+    if (L.split.ns > 1 || L.split.halves > 0) {
       L.spl = off; off = round_up(off + L.split.ws_bytes);
     }
   }
@@ -197,7 +197,8 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   const void *q = a.q, *k = a.k, *v = a.v;
   Layout L = plan_layout(a, mode, dtype, force_decode);
   // A workspace too small for the split prefill runs it unsplit.
-  if (L.split.ns > 1 && workspace_bytes < L.total) L = plan_layout(a, mode, dtype, force_decode, false);
+  if ((L.split.ns > 1 || L.split.halves > 0) && workspace_bytes < L.total)
+    L = plan_layout(a, mode, dtype, force_decode, false);
   if (L.total > 0) {
     if (workspace_bytes < L.total) return ATTN_E_WORKSPACE;
     if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) != 0) return ATTN_E_INVALID;
@@ -262,7 +263,8 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   if (L.decode)
     e = launch_decode(a, L.plan, elem, out_f32, ws + L.dec, s);
   else
-    e = launch_prefill(a, elem, out_f32, L.split, L.split.ns > 1 ? ws + L.spl : nullptr, s);
+    e = launch_prefill(a, elem, out_f32, L.split,
+                       L.split.ns > 1 || L.split.halves > 0 ? ws + L.spl : nullptr, s);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -494,8 +496,8 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int
     p.kernel = ATTN_KERNEL_PREFILL;
     p.waves = prefill_waves(a);
     p.rows = 32 * p.waves;
-    p.splits = L.split.ns;
-    p.workgroups = (long long)B * Hq * ((Nq + p.rows - 1) / p.rows) * L.split.ns;
+    p.splits = L.split.halves > 0 ? 2 : L.split.ns;
+    p.workgroups = (long long)B * Hq * ((Nq + p.rows - 1) / p.rows) * L.split.ns + L.split.halves;
     p.pre_launches = (dtype == ATTN_DT_F32 ? 3 : 0) + (rope ? 1 : 0);
   }
   *plan = p;

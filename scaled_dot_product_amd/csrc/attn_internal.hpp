@@ -57,7 +57,9 @@ KeyRange key_range(const FwdArgs& a);
 // partial (O / l in the output type, m and l in fp32) and the last part of a
 // query tile to arrive merges them.
 struct PrefillSplit {
-  int ns = 1;              // parts per query tile
+  int ns = 1;              // parts per query tile (merged by the last to arrive)
+  int halves = 0;          // or: the last `halves` tiles run as two halves each,
+                           // merged by a second launch (the balanced schedule)
   int64_t tiles = 0;       // query tiles (the unsplit grid)
   int rows = 0;            // query rows per tile
   size_t ctr_bytes = 0;    // arrival counters, one per query tile

@@ -363,7 +363,7 @@ def test_dispatch_of_the_five_workloads(lib):
         # name: (kernel, waves, rows, splits, workgroups, pre_launches)
         "tiny_fp32_256": (sdpa.KERNEL_PREFILL, 4, 128, 2, 8, 3),
         "gqa_decode_f16_4096": (sdpa.KERNEL_DECODE, 4, 8, 16, 128, 0),
-        "sdxl_1024px_bf16": (sdpa.KERNEL_PREFILL, 4, 128, 1, 640, 0),
+        "sdxl_1024px_bf16": (sdpa.KERNEL_PREFILL, 4, 128, 2, 768, 0),
         "video_dit_bf16_32760": (sdpa.KERNEL_PREFILL, 8, 256, 1, 5120, 0),
         "video_dit_quant_32760": (sdpa.KERNEL_PREFILL_QUANT, 4, 128, 1, 10240, 3),
     }
@@ -397,9 +397,21 @@ def test_prefill_split_policy(lib):
     assert (p.splits, p.workgroups) == (2, 256)
     p = _plan(B=1, Hq=129, Hkv=1, Nq=128, Nk=4096, D=64)
     assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 129, 0)
-    # SDXL (640 tiles) runs unsplit
-    p = _plan(B=2, Hq=10, Hkv=10, Nq=4096, Nk=4096, D=64)
-    assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 640, 0)
+    # between half a round and one round of workgroups (768 slots at head dim 64,
+    # 512 at 128): slots - tiles tiles run as two halves, the jobs fill the slots,
+    # a second launch merges; the workspace holds the halves' partials
+    p = _plan(B=2, Hq=10, Hkv=10, Nq=4096, Nk=4096, D=64)      # SDXL: 640 tiles
+    assert (p.splits, p.workgroups) == (2, 768)
+    assert p.workspace_bytes == 128 * 2 * 128 * (64 * 2 + 8)
+    assert _plan(B=1, Hq=767, Hkv=1, Nq=128, Nk=4096, D=64).workgroups == 768
+    assert _plan(B=1, Hq=385, Hkv=1, Nq=128, Nk=4096, D=64).workgroups == 768
+    p = _plan(B=1, Hq=384, Hkv=1, Nq=128, Nk=4096, D=64)      # half a round: unsplit
+    assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 384, 0)
+    p = _plan(B=1, Hq=768, Hkv=1, Nq=128, Nk=4096, D=64)      # a full round: unsplit
+    assert (p.splits, p.workgroups, p.workspace_bytes) == (1, 768, 0)
+    p = _plan(B=1, Hq=300, Hkv=3, Nq=128, Nk=4096, D=128)
+    assert (p.splits, p.workgroups) == (2, 512)
+    assert _plan(B=1, Hq=300, Hkv=3, Nq=128, Nk=64, D=128).splits == 1     # one key tile
     # 85 tiles -> 3 parts; head dim 128 the same
     assert _plan(B=1, Hq=85, Hkv=1, Nq=128, Nk=4096, D=128).splits == 3
     # parts keep >= 2 key tiles each

@@ -1,7 +1,9 @@
-"""The split prefill: a grid of at most 128 query tiles runs each query
-tile's key range as 2-4 workgroups; each publishes its normalised
-partial (O / l in the output type, m and l in fp32) and the last one of the
-tile to arrive merges them with log-sum-exp weights. Checked against the
+"""The split prefill. A grid of at most 128 query tiles runs each query
+tile's key range as 2-4 workgroups; each publishes its normalised partial
+(O / l in the output type, m and l in fp32) and the last one of the tile to
+arrive merges them with log-sum-exp weights. A grid between half a round and
+one round of workgroups runs enough tiles in two halves that the jobs fill
+the slots, and a second launch merges the halves. Checked against the
 oracle, against the unsplit schedule of the same call (a workspace too small
 for the split runs it unsplit), with garbage left in the workspace, and under
 graph replay."""
@@ -28,6 +30,12 @@ SPLIT = [
     (1, 4, 4, 512, 8192, 128, bf16, False, 0, 0, 4),       # head dim 128, long keys
     (2, 2, 2, 2048, 2048, 128, f16, True, 0, 0, 4),        # causal square, 64 tiles
     (1, 85, 85, 128, 1000, 64, bf16, False, 0, 0, 3),      # 85 tiles -> 3 parts
+    # the balanced schedule (between half a round and one round of workgroups):
+    # slots - tiles tiles in two halves, merged by a second launch
+    (2, 10, 10, 4096, 4096, 64, bf16, False, 0, 0, 2),     # SDXL: 640 tiles, 128 in halves
+    (1, 20, 5, 2560, 2560, 64, f16, True, 0, 0, 2),        # causal, 400 tiles, 368 in halves
+    (1, 300, 3, 128, 1000, 128, bf16, False, 0, 0, 2),     # head dim 128: 300 tiles on 512 slots
+    (1, 50, 50, 1000, 700, 64, f32, True, 200, 100, 2),    # fp32, window, ragged q and k tiles
 ]
 
 
@@ -113,8 +121,9 @@ def test_split_prefill_garbage_workspace_and_reuse():
             assert torch.equal(out, ref), (fill, rep)
 
 
-def test_split_prefill_graph_replays_match_eager():
-    w, q, k, v = _case_dev(SPLIT[0])
+@pytest.mark.parametrize("which", [0, 7], ids=["fused-merge", "balanced"])
+def test_split_prefill_graph_replays_match_eager(which):
+    w, q, k, v = _case_dev(SPLIT[which])
     n = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, dtype=w.dtype)
     ws = torch.empty(n, dtype=torch.uint8, device=q.device)
     out = torch.empty_like(q)
