@@ -605,39 +605,40 @@ prefill_kernel(FwdArgs a, int ntq, SplitArgs sp) {
   }
 }
 
-// The balanced schedule's merge: one workgroup per tile run in halves, one
-// thread per (row, 4 channels): weights 2^(m_s - M) l_s, O = the weighted
-// sum of the two normalised halves over the sum of the weights.
+// The balanced schedule's merge: one thread per (row, 4 channels) of the
+// tiles run in halves (all their loads in flight at once): weights
+// 2^(m_s - M) l_s, O = the weighted sum of the two normalised halves over the
+// sum of the weights.
 template <typename TO, int D>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(FwdArgs a, int ntq, int rows, int first,
-                                                            SplitArgs sp) {
-  const int sidx = blockIdx.x;
+                                                            int halves, SplitArgs sp) {
+  constexpr int CH = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)halves * rows * CH) return;
+  const int sidx = (int)(idx / (rows * CH));
+  const int rem = (int)(idx - (int64_t)sidx * rows * CH);
+  const int n = rem / CH, d = (rem - n * CH) * 4;
   const int tile = first + sidx;
   const int bh = tile / ntq, qt_in = tile - bh * ntq;
   const int qt = a.causal ? ntq - 1 - qt_in : qt_in;
-  const int q0 = qt * rows;
-  constexpr int CH = D / 4;
+  const int qrow = qt * rows + n;
+  if (qrow >= a.Nq) return;
   const TO* op = (const TO*)sp.opart;
-  for (int idx = threadIdx.x; idx < rows * CH; idx += blockDim.x) {
-    const int n = idx / CH, d = (idx - n * CH) * 4;
-    const int qrow = q0 + n;
-    if (qrow >= a.Nq) continue;
-    const int64_t r0 = (int64_t)sidx * 2 * rows + n, r1 = r0 + rows;
-    const float m0 = sp.mlpart[2 * r0], l0 = sp.mlpart[2 * r0 + 1];
-    const float m1 = sp.mlpart[2 * r1], l1 = sp.mlpart[2 * r1 + 1];
-    const float M = fmaxf(m0, m1);
-    // a half with no visible key has m = -inf and weight 0
-    const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * l0;
-    const float w1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M) * l1;
-    const float L = w0 + w1;
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float v0[4], v1[4], o[4];
-    get4<TO>(op + r0 * D + d, v0);
-    get4<TO>(op + r1 * D + d, v1);
+  const int64_t r0 = (int64_t)sidx * 2 * rows + n, r1 = r0 + rows;
+  const float m0 = sp.mlpart[2 * r0], l0 = sp.mlpart[2 * r0 + 1];
+  const float m1 = sp.mlpart[2 * r1], l1 = sp.mlpart[2 * r1 + 1];
+  float v0[4], v1[4], o[4];
+  get4<TO>(op + r0 * D + d, v0);
+  get4<TO>(op + r1 * D + d, v1);
+  const float M = fmaxf(m0, m1);
+  // a half with no visible key has m = -inf and weight 0
+  const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M) * l0;
+  const float w1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M) * l1;
+  const float L = w0 + w1;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = fmaf(w1, v1[c], w0 * v0[c]) * inv;
-    put4<TO>((TO*)a.o + ((int64_t)bh * a.Nq + qrow) * D + d, o);
-  }
+  for (int c = 0; c < 4; ++c) o[c] = fmaf(w1, v1[c], w0 * v0[c]) * inv;
+  put4<TO>((TO*)a.o + ((int64_t)bh * a.Nq + qrow) * D + d, o);
 }
 
 template <typename T, typename TO, int D, int W>
@@ -663,8 +664,9 @@ hipError_t launch_w(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStrea
   if (sp.halves > 0) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_merge_kernel<TO, D>), dim3((unsigned)sp.halves), dim3(256), 0, s, a,
-                       ntq, BM, (int)(tiles - sp.halves), sp);
+    const int64_t items = (int64_t)sp.halves * BM * (D / 4);
+    hipLaunchKernelGGL((prefill_merge_kernel<TO, D>), dim3((unsigned)((items + 255) / 256)), dim3(256),
+                       0, s, a, ntq, BM, (int)(tiles - sp.halves), sp.halves, sp);
   }
   return hipGetLastError();
 }
