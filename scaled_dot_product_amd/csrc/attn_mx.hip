@@ -373,7 +373,8 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       Cm[mb] = C + (float)E[mb];   // exact: C's ulp is below 1 and E an integer
     }
 
-    // S of tile i + 1 beside the weights of tile i.
+    // S of tile i + 1 after the weights of tile i (K operand reads, vector
+    // work, then the MFMAs; the other wave of the SIMD fills the gaps).
     s_mma((i + 1) & 1, nxt);
     i32x8 pb;
 #pragma unroll
@@ -391,6 +392,9 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
         pb[4 * mb + q4] = pk;
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 80, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
     const int psc = (half ? E[1] : E[0]) + 127;   // lane half h: scale of block h
     // The denominator: the tile's row sums of the weights the numerator uses,
     // in unscaled units, from one more scaled MFMA against an all-ones block
