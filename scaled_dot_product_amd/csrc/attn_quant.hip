@@ -207,9 +207,10 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
 
 // ---------------------------------------------------------------------------
 // Quantised prefill: 4 waves x 32 query rows, 64-key tiles, two workgroups
-// per CU, software-pipelined like the exact kernel (S of tile i+1 on the
-// matrix cores while the exponentials of tile i run; code tiles go straight
-// from HBM into XOR-swizzled LDS tiles).
+// per CU, software-pipelined like the exact kernel (S of tile i+1 issued
+// right after the exponentials of tile i, while the SIMD's other wave runs
+// its own vector work; code tiles go straight from HBM into XOR-swizzled LDS
+// tiles).
 //
 // The V block scale s_v changes from tile to tile. Rather than rescale the
 // fp32 output by s_v after every tile, each tile's weights are quantised as
