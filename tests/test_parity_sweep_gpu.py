@@ -1,0 +1,86 @@
+"""A seeded sweep of small random shapes through attn_fwd / attn_fwd_sliding,
+every output row against the fp64 oracle.
+
+The hand-picked cases elsewhere pin the corners one by one; this sweep draws
+the arguments together (batch, GQA group, ragged query and key counts, head
+dimension, dtype, causal offset, shared lower bound or per-row window, exact /
+INT8-QK FP8-PV / MX mode, and few-row shapes that dispatch to the split-KV
+decode), so that combinations nobody wrote down are run too. The cases are a
+fixed function of the seed below; the inputs come from the shared seeded
+generators.
+"""
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_amd as sdpa
+from scaled_dot_product_amd.inputs import Workload
+
+from _parity import check_workload, masked_rows
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20261203
+N_CASES = 120
+
+
+def _cases():
+    rng = np.random.RandomState(SEED)
+    out = []
+    for n in range(N_CASES):
+        mode = int(rng.choice([0, 0, 0, 1, 2]))
+        dts = [torch.bfloat16, torch.float16] + ([torch.float32] if mode == 0 else [])
+        dt = dts[int(rng.randint(len(dts)))]
+        D = int(rng.choice([64, 128]))
+        B = int(rng.choice([1, 2]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 4]))
+        if rng.rand() < 0.25:
+            # few rows per KV head over a long range: the split-KV decode
+            Nq = int(rng.randint(1, 32 // G + 1))
+            Nk = int(rng.randint(512, 2000))
+        else:
+            Nq = int(rng.randint(1, 300))
+            Nk = int(rng.randint(64 if mode else 1, 700))
+        causal = bool(rng.rand() < 0.5)
+        pos0 = int(rng.choice([0, max(0, Nk - Nq), rng.randint(0, Nk)])) if causal else 0
+        kind = rng.choice(["none", "lo", "w"])
+        window_lo = int(rng.randint(0, Nk)) if kind == "lo" else 0
+        window_w = int(rng.randint(1, Nk + 1)) if kind == "w" else 0
+        if kind == "w" and not causal:
+            pos0 = int(rng.randint(0, Nk))
+        out.append(Workload(f"sweep{n}", B, Hkv * G, Hkv, Nq, Nk, D, dt, causal=causal,
+                            window_lo=window_lo, pos0=pos0, mode=mode, window_w=window_w))
+    return out
+
+
+CASES = _cases()
+
+
+def _id(w):
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype]
+    return (f"{w.name}-m{w.mode}-{dt}-D{w.D}-B{w.B}-H{w.Hq}x{w.Hkv}-{w.Nq}x{w.Nk}"
+            f"{'-c' if w.causal else ''}-p{w.pos0}-lo{w.window_lo}-w{w.window_w}")
+
+
+def test_sweep_covers_every_kernel():
+    # the draw reaches every mode, both head dimensions, every dtype, the
+    # per-row window and the decode dispatch
+    kinds = set()
+    for w in CASES:
+        if w.mode == 0 and w.window_w == 0:
+            p = sdpa.plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=w.causal,
+                          window_lo=w.window_lo, pos0=w.pos0, dtype=w.dtype)
+            kinds.add(p.kernel)
+    assert {w.mode for w in CASES} == {0, 1, 2}
+    assert {w.D for w in CASES} == {64, 128}
+    assert {w.dtype for w in CASES} == {torch.bfloat16, torch.float16, torch.float32}
+    assert any(w.window_w > 0 for w in CASES) and any(w.window_lo > 0 for w in CASES)
+    assert sdpa.KERNEL_DECODE in kinds and sdpa.KERNEL_PREFILL in kinds
+
+
+@pytest.mark.parametrize("w", CASES, ids=[_id(w) for w in CASES])
+def test_sweep_case_matches_oracle(w):
+    out, _, _, _ = check_workload(w)
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
