@@ -658,6 +658,10 @@ def ab_part(part):
     if part == "causal":
         w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_causal_bf16_32760", causal=True)
         return "ms", lambda: bench_prefill(w, 8, 1)
+    if part == "sliding":
+        w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_sliding4096_bf16_32760",
+                                                      causal=True, window_w=4096)
+        return "ms", lambda: bench_prefill(w, 10, 1)
     if part == "sdxl":
         w = WORKLOADS["sdxl_1024px_bf16"]
         return "us", lambda: bench_prefill(w, 200, 10) * 1e3
