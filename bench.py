@@ -686,7 +686,6 @@ def ab_part(part):
 def run_ab(lib_a, lib_b, part, pairs, seed=1):
     """Paired A/B of two library builds: blocks in the order A B, B A, A B, ...
     (pair 0 discarded), bootstrap 95 % interval of the mean ratio B / A."""
-    import numpy as np
     import scaled_dot_product_amd as sdpa
     handles = {"A": sdpa.open_library(lib_a), "B": sdpa.open_library(lib_b)}
     unit, fn = ab_part(part)
@@ -699,14 +698,25 @@ def run_ab(lib_a, lib_b, part, pairs, seed=1):
             times[key].append(t)
         log(f"ab {part} pair {i}: A {times['A'][-1]:.4f} {unit}, B {times['B'][-1]:.4f} {unit}"
             + (" (discarded)" if i == 0 else ""))
-    a = np.array(times["A"][1:])
-    b = np.array(times["B"][1:])
+    rec = ab_stats(times["A"][1:], times["B"][1:], seed)
+    return {"ab": part, "unit": unit, "lib_a": lib_a, "lib_b": lib_b, **rec}
+
+
+def ab_stats(a, b, seed=1, boots=4000):
+    """Paired times of A and B (one entry per block pair) -> mean ratio B / A,
+    its bootstrap 95 % interval (pairs resampled with replacement) and the
+    verdict: a change only when the whole interval lies on one side of 1."""
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size == 0 or a.shape != b.shape:
+        raise ValueError("need the same positive number of A and B times")
     ratio = b / a
     rng = np.random.default_rng(seed)
-    boots = np.array([ratio[rng.integers(0, ratio.size, ratio.size)].mean() for _ in range(4000)])
-    lo, hi = np.percentile(boots, [2.5, 97.5])
+    means = np.array([ratio[rng.integers(0, ratio.size, ratio.size)].mean() for _ in range(boots)])
+    lo, hi = np.percentile(means, [2.5, 97.5])
     verdict = "B faster" if hi < 1.0 else ("B slower" if lo > 1.0 else "no difference")
-    return {"ab": part, "unit": unit, "lib_a": lib_a, "lib_b": lib_b, "pairs": int(ratio.size),
+    return {"pairs": int(ratio.size),
             "a_median": round(float(np.median(a)), 4), "b_median": round(float(np.median(b)), 4),
             "ratio_b_over_a": round(float(ratio.mean()), 4),
             "ci95": [round(float(lo), 4), round(float(hi), 4)], "verdict": verdict}
