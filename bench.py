@@ -297,8 +297,9 @@ def load_probe():
         lib.attn_probe_empty.argtypes = [i, vp]
         lib.attn_probe_valu.argtypes = [i, i, i, vp, vp]
         lib.attn_probe_mix.argtypes = [i, i, i, vp, vp]
+        lib.attn_probe_phase.argtypes = [i, i, i, i, vp, vp]
         for f in (lib.attn_probe_mfma, lib.attn_probe_read, lib.attn_probe_empty,
-                  lib.attn_probe_valu, lib.attn_probe_mix):
+                  lib.attn_probe_valu, lib.attn_probe_mix, lib.attn_probe_phase):
             f.restype = i
         _PROBE = lib
     return _PROBE
@@ -336,6 +337,8 @@ def measured_peaks():
 
 VALU_KINDS = ("v_exp_f32", "v_fma_f32", "v_cvt_pk_bf16_f32", "v_cvt_pk_fp8_f32", "v_max3_f32",
               "v_dot2c_f32_bf16")
+PHASE_KINDS = ("96 vector + 16 MFMA", "96 vector only", "16 MFMA only", "48 vector + 16 MFMA",
+               "144 vector + 16 MFMA")
 
 
 def valu_costs():
@@ -367,10 +370,23 @@ def valu_costs():
         base = per if nv == 0 else base
         mix[str(nv / 4)] = {"ns_per_mfma_per_simd": round(per, 3),
                             "mfma_rate_pct": round(100 * base / per, 1)}
+    # two waves per SIMD alternating vector and matrix blocks between barriers:
+    # every wave in the same order, or the SIMD's second wave matrix-first
+    phase = {}
+    out8 = torch.empty(cus * 512, dtype=torch.float32, device="cuda:0")
+    for kind, name in enumerate(PHASE_KINDS):
+        for late in (0, 1):
+            if late and kind in (1, 2):
+                continue
+            ms = time_events(lambda: _probe_call(probe.attn_probe_phase(kind, late, iters, cus,
+                                                                        out8.data_ptr(), stream),
+                                                 "attn_probe_phase"), 3, 1)
+            phase[name + (", second wave matrix-first" if late else "")] = round(ms * 1e6 / iters, 1)
     log(f"vector instruction costs: {costs}")
     log(f"MFMA rate beside vector work (vector instructions per MFMA -> % of MFMA-only): "
         f"{ {k: v['mfma_rate_pct'] for k, v in mix.items()} }")
-    return {"valu_costs": costs, "mfma_beside_valu": mix}
+    log(f"vector/matrix blocks, ns per round (two waves per SIMD): {phase}")
+    return {"valu_costs": costs, "mfma_beside_valu": mix, "phase_ns_per_round": phase}
 
 
 def graph_us_per_call(calls, reps=20):

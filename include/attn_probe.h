@@ -62,6 +62,19 @@ int attn_probe_valu(int kind, int iters, int blocks, float* out, void* stream);
  * 1..65535. */
 int attn_probe_mix(int nv, int iters, int blocks, float* out, void* stream);
 
+/* Whether two waves of one SIMD gain from running opposite phases: `blocks`
+ * workgroups of 8 waves (two per SIMD), each wave `iters` rounds of a vector
+ * block (v_exp_f32 and v_fma_f32 in the ratio 1 : 2, 16 chains) and a matrix
+ * block (v_mfma_f32_32x32x16_bf16 on four accumulators), then a workgroup
+ * barrier. late = 0: every wave runs vector then matrix; late = 1: waves 4..7
+ * (the second wave of each SIMD) run matrix then vector.
+ *   kind 0: 96 vector + 16 MFMA   1: 96 vector only   2: 16 MFMA only
+ *   kind 3: 48 vector + 16 MFMA   4: 144 vector + 16 MFMA
+ *   out: blocks * 512 floats (4-byte aligned).
+ * Invalid: out NULL or misaligned, kind outside 0..4, late not 0 or 1,
+ * iters < 1, blocks outside 1..65535. */
+int attn_probe_phase(int kind, int late, int iters, int blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

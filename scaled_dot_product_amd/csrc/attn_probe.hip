@@ -15,6 +15,10 @@
 //                     three-way maximum, bf16 pair dot product
 //   attn_probe_mix    the bf16 MFMA rate with nv vector instructions (one
 //                     exponential to two FMAs) issued beside every 4 MFMAs
+//   attn_probe_phase  two waves per SIMD alternating a block of vector work
+//                     and a block of MFMAs between workgroup barriers, all
+//                     in the same order or the second wave of each SIMD in
+//                     the opposite order (matrix block first)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -177,6 +181,57 @@ __global__ void __launch_bounds__(256) probe_mix_kernel(float* out, int iters) {
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+// 8 waves (two per SIMD); per round a vector block of NV instructions (one
+// v_exp_f32 to two v_fma_f32 on 16 chains) and a matrix block of NM
+// v_mfma_f32_32x32x16_bf16 on four accumulators, then a barrier. Waves 4..7
+// (the second wave of each SIMD) run the matrix block first when late != 0.
+template <int NV, int NM>
+__global__ void __launch_bounds__(512) probe_phase_kernel(float* out, int iters, int late) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (lane + i));
+    b[i] = (__bf16)(0.002f * (i - lane));
+  }
+  float r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = 0.37f * (i + 1) + 1e-3f * threadIdx.x;
+  f32x16 c[4] = {};
+  const bool mfirst = late != 0 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= 4;
+  auto vblock = [&]() {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i % 3 == 0)
+        asm volatile("v_exp_f32 %0, %0" : "+v"(r[i & 15]));
+      else
+        asm volatile("v_fma_f32 %0, %0, %0, %0" : "+v"(r[i & 15]));
+    }
+  };
+  auto mblock = [&]() {
+#pragma unroll
+    for (int k = 0; k < NM; ++k) c[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k & 3], 0, 0, 0);
+  };
+  for (int it = 0; it < iters; ++it) {
+    if (mfirst) {
+      mblock();
+      vblock();
+    } else {
+      vblock();
+      mblock();
+    }
+    __syncthreads();
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += c[k][j];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += r[i];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 }  // namespace attn
@@ -234,6 +289,22 @@ int attn_probe_mix(int nv, int iters, int blocks, float* out, void* stream) {
     case 16: hipLaunchKernelGGL((attn::probe_mix_kernel<16>), dim3(blocks), dim3(256), 0, s, out, iters); break;
     case 24: hipLaunchKernelGGL((attn::probe_mix_kernel<24>), dim3(blocks), dim3(256), 0, s, out, iters); break;
     case 32: hipLaunchKernelGGL((attn::probe_mix_kernel<32>), dim3(blocks), dim3(256), 0, s, out, iters); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int attn_probe_phase(int kind, int late, int iters, int blocks, float* out, void* stream) {
+  if (out == nullptr || ((uintptr_t)out & 3u) || iters < 1 || blocks < 1 || blocks > 65535 ||
+      (late != 0 && late != 1))
+    return -1;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((attn::probe_phase_kernel<96, 16>), dim3(blocks), dim3(512), 0, s, out, iters, late); break;
+    case 1: hipLaunchKernelGGL((attn::probe_phase_kernel<96, 0>), dim3(blocks), dim3(512), 0, s, out, iters, late); break;
+    case 2: hipLaunchKernelGGL((attn::probe_phase_kernel<0, 16>), dim3(blocks), dim3(512), 0, s, out, iters, late); break;
+    case 3: hipLaunchKernelGGL((attn::probe_phase_kernel<48, 16>), dim3(blocks), dim3(512), 0, s, out, iters, late); break;
+    case 4: hipLaunchKernelGGL((attn::probe_phase_kernel<144, 16>), dim3(blocks), dim3(512), 0, s, out, iters, late); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;

@@ -41,6 +41,7 @@ def probe(lib):
     p.attn_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
     p.attn_probe_valu.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
     p.attn_probe_mix.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    p.attn_probe_phase.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
     return p
 
 
@@ -55,8 +56,8 @@ def test_header_declares_the_boundary():
         assert n in names
     assert "attn_probe_mfma" not in names     # measurement probes live in their own library
     assert _declared_functions(PROBE_HEADER) == ["attn_probe_empty", "attn_probe_mfma",
-                                                 "attn_probe_mix", "attn_probe_read",
-                                                 "attn_probe_valu"]
+                                                 "attn_probe_mix", "attn_probe_phase",
+                                                 "attn_probe_read", "attn_probe_valu"]
 
 
 def test_library_exports_every_declared_symbol(lib, probe):
@@ -255,6 +256,13 @@ def test_probe_rejects_before_enqueue(probe):
     assert m(5, 4, 2, FAKE, None) == E_INVALID          # not a built vector count
     assert m(8, 0, 2, FAKE, None) == E_INVALID
     assert m(8, 4, 0, FAKE, None) == E_INVALID
+    ph = probe.attn_probe_phase
+    assert ph(0, 0, 4, 2, None, None) == E_INVALID
+    assert ph(0, 0, 4, 2, FAKE + 2, None) == E_INVALID   # misaligned
+    assert ph(5, 0, 4, 2, FAKE, None) == E_INVALID       # unknown kind
+    assert ph(0, 2, 4, 2, FAKE, None) == E_INVALID       # late is 0 or 1
+    assert ph(0, 1, 0, 2, FAKE, None) == E_INVALID
+    assert ph(0, 1, 4, 65536, FAKE, None) == E_INVALID
 
 
 def test_mx_entry_points_reject_before_enqueue(lib):

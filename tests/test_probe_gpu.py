@@ -59,3 +59,15 @@ def test_probe_mix_runs(nv):
     torch.cuda.synchronize()
     assert st == 0
     assert (out.view(torch.int32) != torch.tensor(float("nan")).view(torch.int32).item()).all()
+
+
+@pytest.mark.parametrize("kind", range(5))
+@pytest.mark.parametrize("late", [0, 1])
+def test_probe_phase_runs(kind, late):
+    blocks = 4
+    out = torch.full((blocks * 512,), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = bench.load_probe().attn_probe_phase(kind, late, 4, blocks, out.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert (out.view(torch.int32) != torch.tensor(float("nan")).view(torch.int32).item()).all()
