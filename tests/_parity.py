@@ -81,3 +81,35 @@ def masked_rows(w):
         if hi < lo:
             out.append(i)
     return out
+
+
+def check_rope(w, rope, rows=None):
+    """Run w through attn_fwd_rope with the rotary embedding rope (keyword
+    arguments of sdpa.Rope) and compare with the oracle, which turns Q and K
+    in double precision and then takes exact attention."""
+    announce(f"rope {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} {w.dtype} "
+             f"causal={w.causal} window_lo={w.window_lo} pos0={w.pos0} mode={w.mode} rope={rope}")
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    out = sdpa.fwd_rope(q.to(dev), k.to(dev), v.to(dev), sdpa.Rope(**rope), causal=w.causal,
+                        window_lo=w.window_lo, pos0=w.pos0, scale=w.scale, mode=w.mode)
+    torch.cuda.synchronize()
+    out = out.double().cpu()
+    assert torch.isfinite(out).all()
+    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, **rope)
+    if rows is None:
+        ref = oracle.attn_rope(q, k, v, **kw)
+        got = out.numpy()
+    else:
+        ref = oracle.attn_rope(q, k, v, rows=rows, **kw)
+        got = out.reshape(-1, w.D)[torch.from_numpy(rows)].numpy()
+    rel, mabs = metrics(got, ref)
+    print(f"    rel={rel:.3e} max_abs={mabs:.3e}", flush=True)
+    if w.mode == 0:
+        assert rel <= EXACT_REL, rel
+        assert mabs <= EXACT_ABS, mabs
+    else:
+        assert rel <= QUANT_REL, rel
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
+    return out, ref, rel, mabs

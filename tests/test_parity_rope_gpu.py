@@ -3,15 +3,13 @@ C ABI, against the fp64 oracle (which turns Q and K in double precision and
 then takes exact attention). The exact mode is held to the exact-mode bar; the
 rotated Q and K are rounded to the operand type once more than in the oracle,
 well inside it. The quantised and MX modes are held to their 6e-2."""
-import numpy as np
 import pytest
 import torch
 
-import oracle
 import scaled_dot_product_amd as sdpa
-from scaled_dot_product_amd.inputs import WORKLOADS, Workload, make_qkv, sample_rows
+from scaled_dot_product_amd.inputs import WORKLOADS, Workload, sample_rows
 
-from _parity import EXACT_ABS, EXACT_REL, QUANT_REL, announce, masked_rows, metrics
+from _parity import check_rope
 
 pytestmark = pytest.mark.gpu
 
@@ -27,32 +25,7 @@ def _lib():
 
 
 def _check(w, rope, rows=None):
-    announce(f"rope {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} {w.dtype} "
-             f"causal={w.causal} window_lo={w.window_lo} pos0={w.pos0} mode={w.mode} rope={rope}")
-    q, k, v = make_qkv(w)
-    dev = torch.device("cuda:0")
-    r = sdpa.Rope(**rope)
-    out = sdpa.fwd_rope(q.to(dev), k.to(dev), v.to(dev), r, causal=w.causal, window_lo=w.window_lo,
-                        pos0=w.pos0, scale=w.scale, mode=w.mode)
-    torch.cuda.synchronize()
-    out = out.double().cpu()
-    assert torch.isfinite(out).all()
-    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0, **rope)
-    if rows is None:
-        ref = oracle.attn_rope(q, k, v, **kw)
-        got = out.numpy()
-    else:
-        ref = oracle.attn_rope(q, k, v, rows=rows, **kw)
-        got = out.reshape(-1, w.D)[torch.from_numpy(rows)].numpy()
-    rel, mabs = metrics(got, ref)
-    print(f"    rel={rel:.3e} max_abs={mabs:.3e}", flush=True)
-    if w.mode == 0:
-        assert rel <= EXACT_REL, rel
-        assert mabs <= EXACT_ABS, mabs
-    else:
-        assert rel <= QUANT_REL, rel
-    for i in masked_rows(w):
-        assert torch.all(out[:, :, i] == 0), i
+    check_rope(w, rope, rows)
 
 
 ROPES = [

@@ -1,5 +1,6 @@
-"""A seeded sweep of small random shapes through attn_fwd / attn_fwd_sliding,
-every output row against the fp64 oracle.
+"""A seeded sweep of small random shapes through attn_fwd / attn_fwd_sliding
+(and attn_fwd_rope with random rotary settings), every output row against the
+fp64 oracle.
 
 The hand-picked cases elsewhere pin the corners one by one; this sweep draws
 the arguments together (batch, GQA group, ragged query and key counts, head
@@ -16,7 +17,7 @@ import torch
 import scaled_dot_product_amd as sdpa
 from scaled_dot_product_amd.inputs import Workload
 
-from _parity import check_workload, masked_rows
+from _parity import check_rope, check_workload, masked_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +85,46 @@ def test_sweep_case_matches_oracle(w):
     out, _, _, _ = check_workload(w)
     for i in masked_rows(w):
         assert torch.all(out[:, :, i] == 0), i
+
+
+N_ROPE = 30
+
+
+def _rope_cases():
+    rng = np.random.RandomState(SEED + 1)
+    out = []
+    for n in range(N_ROPE):
+        mode = int(rng.choice([0, 0, 1, 2]))
+        dts = [torch.bfloat16, torch.float16] + ([torch.float32] if mode == 0 else [])
+        dt = dts[int(rng.randint(len(dts)))]
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        if rng.rand() < 0.25:
+            Nq, Nk = int(rng.randint(1, 32 // G + 1)), int(rng.randint(512, 1500))
+        else:
+            Nq, Nk = int(rng.randint(1, 260)), int(rng.randint(64 if mode else 1, 600))
+        causal = bool(rng.rand() < 0.5)
+        pos0 = int(rng.choice([0, max(0, Nk - Nq), rng.randint(0, Nk)])) if causal else 0
+        window_lo = int(rng.randint(0, Nk)) if rng.rand() < 0.3 else 0
+        scaling = int(rng.choice([0, 1, 2]))
+        rope = dict(style=int(rng.choice([0, 1])), scaling=scaling,
+                    base=float(rng.choice([10000.0, 500000.0])))
+        if scaling:
+            rope["factor"] = float(rng.choice([2.0, 4.0, 8.0]))
+        if scaling == 2:
+            rope.update(orig_ctx=int(rng.choice([64, 256, 1024])), beta_fast=32.0, beta_slow=1.0)
+        w = Workload(f"rope_sweep{n}", int(rng.choice([1, 2])), Hkv * G, Hkv, Nq, Nk, D, dt,
+                     causal=causal, window_lo=window_lo, pos0=pos0, mode=mode)
+        out.append((w, rope))
+    return out
+
+
+ROPE_CASES = _rope_cases()
+
+
+@pytest.mark.parametrize("case", ROPE_CASES,
+                         ids=[f"{_id(w)}-s{r['style']}{r['scaling']}" for w, r in ROPE_CASES])
+def test_sweep_rope_case_matches_oracle(case):
+    w, rope = case
+    check_rope(w, rope)
