@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import scaled_dot_product_amd as sdpa
-from scaled_dot_product_amd.inputs import make_qkv, sample_rows
+from scaled_dot_product_amd.inputs import make_kv_codes, make_qkv, normal, sample_rows
 
 # Tolerances stated for the path: exact mode rel-RMS <= 1e-2 and max-abs <= 2e-2,
 # quantised mode rel-L2 <= 6e-2, both against the fp64 oracle.
@@ -113,3 +113,38 @@ def check_rope(w, rope, rows=None):
     for i in masked_rows(w):
         assert torch.all(out[:, :, i] == 0), i
     return out, ref, rel, mabs
+
+
+# Quantised-cache decode: against the oracle with Q through its own INT8
+# codes the only difference is the E4M3 rounding of the weights (each off by
+# at most 2^-4 relative, about 2^-4/sqrt(3) in RMS over many keys); KVQ_REL
+# leaves a margin over that. Against exact attention on the dequantised cache
+# the INT8 rounding of Q is added, held to QUANT_REL.
+KVQ_REL = 4e-2
+
+
+def check_kvq(w, q=None, cache=None, **kw_run):
+    """attn_decode_kvq on w's seeded quantised cache against both oracles."""
+    announce(f"kvq {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} "
+             f"{w.dtype} causal={w.causal} window_lo={w.window_lo} pos0={w.pos0}")
+    q = q if q is not None else normal(w.q_shape, 41, w.dtype)
+    cache = cache if cache is not None else make_kv_codes(w)
+    dev = torch.device("cuda:0")
+    kc, ks, vc, vs = (t.to(dev) for t in cache)
+    out = sdpa.decode_kvq(q.to(dev), kc, ks, vc, vs, causal=w.causal, window_lo=w.window_lo,
+                          pos0=w.pos0, scale=w.scale, **kw_run)
+    torch.cuda.synchronize()
+    out = out.double().cpu()
+    assert torch.isfinite(out).all()
+    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0)
+    ref_q = oracle.attn_kvq(q, *cache, quant_q=True, **kw)
+    ref = oracle.attn_kvq(q, *cache, quant_q=False, **kw)
+    rel_q, _ = metrics(out.numpy(), ref_q)
+    rel, _ = metrics(out.numpy(), ref)
+    print(f"    rel(vs quantised-Q oracle)={rel_q:.3e} rel(vs exact on the cache)={rel:.3e}",
+          flush=True)
+    assert rel_q <= KVQ_REL, rel_q
+    assert rel <= QUANT_REL, rel
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
+    return out

@@ -7,8 +7,8 @@ kernel's recipe up to the E4M3 rounding of the softmax weights), and exact
 attention over the dequantised cache with Q as given. The bound for the first
 follows from the weight rounding: E4M3 keeps 3 mantissa bits, so each weight
 is off by at most 2^-4 relative and, over many keys, by about 2^-4/sqrt(3) in
-RMS; KVQ_REL = 4e-2 leaves a margin over that. The second adds the INT8
-rounding of Q and is held to the quantised mode's 6e-2.
+RMS; KVQ_REL = 4e-2 (in the shared helpers) leaves a margin over that. The
+second adds the INT8 rounding of Q and is held to the quantised mode's 6e-2.
 """
 import numpy as np
 import pytest
@@ -18,11 +18,9 @@ import oracle
 import scaled_dot_product_amd as sdpa
 from scaled_dot_product_amd.inputs import WORKLOADS, Workload, make_kv_codes, make_qkv, normal
 
-from _parity import QUANT_REL, announce, masked_rows, metrics
+from _parity import QUANT_REL, check_kvq, metrics
 
 pytestmark = pytest.mark.gpu
-
-KVQ_REL = 4e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -41,25 +39,7 @@ def _run(w, q, cache, **kw):
     return out
 
 
-def _check(w, q=None, cache=None):
-    announce(f"kvq {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} D={w.D} "
-             f"{w.dtype} causal={w.causal} window_lo={w.window_lo} pos0={w.pos0}")
-    q = q if q is not None else normal(w.q_shape, 41, w.dtype)
-    cache = cache if cache is not None else make_kv_codes(w)
-    out = _run(w, q, cache).double().cpu()
-    assert torch.isfinite(out).all()
-    kw = dict(scale=w.scale, causal=w.causal, window_lo=w.window_lo, pos0=w.pos0)
-    ref_q = oracle.attn_kvq(q, *cache, quant_q=True, **kw)
-    ref = oracle.attn_kvq(q, *cache, quant_q=False, **kw)
-    rel_q, _ = metrics(out.numpy(), ref_q)
-    rel, _ = metrics(out.numpy(), ref)
-    print(f"    rel(vs quantised-Q oracle)={rel_q:.3e} rel(vs exact on the cache)={rel:.3e}",
-          flush=True)
-    assert rel_q <= KVQ_REL, rel_q
-    assert rel <= QUANT_REL, rel
-    for i in masked_rows(w):
-        assert torch.all(out[:, :, i] == 0), i
-    return out
+_check = check_kvq
 
 
 def test_gqa_decode_kvq_workload():

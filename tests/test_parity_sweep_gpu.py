@@ -1,6 +1,6 @@
 """A seeded sweep of small random shapes through attn_fwd / attn_fwd_sliding
-(and attn_fwd_rope with random rotary settings), every output row against the
-fp64 oracle.
+(and attn_fwd_rope with random rotary settings, and attn_decode_kvq over random
+quantised caches), every output row against the fp64 oracle.
 
 The hand-picked cases elsewhere pin the corners one by one; this sweep draws
 the arguments together (batch, GQA group, ragged query and key counts, head
@@ -17,7 +17,7 @@ import torch
 import scaled_dot_product_amd as sdpa
 from scaled_dot_product_amd.inputs import Workload
 
-from _parity import check_rope, check_workload, masked_rows
+from _parity import check_kvq, check_rope, check_workload, masked_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -128,3 +128,32 @@ ROPE_CASES = _rope_cases()
 def test_sweep_rope_case_matches_oracle(case):
     w, rope = case
     check_rope(w, rope)
+
+
+N_KVQ = 25
+
+
+def _kvq_cases():
+    rng = np.random.RandomState(SEED + 2)
+    out = []
+    for n in range(N_KVQ):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        Nq = int(rng.randint(1, 32 // G + 1))
+        Nk = int(rng.randint(1, 5000))
+        causal = bool(rng.rand() < 0.7)
+        pos0 = int(rng.choice([max(0, Nk - Nq), rng.randint(0, Nk + 50)])) if causal else 0
+        window_lo = int(rng.randint(0, Nk + 20)) if rng.rand() < 0.3 else 0
+        dt = [torch.float16, torch.bfloat16][int(rng.randint(2))]
+        out.append(Workload(f"kvq_sweep{n}", int(rng.choice([1, 2])), Hkv * G, Hkv, Nq, Nk,
+                            int(rng.choice([64, 128])), dt, causal=causal, window_lo=window_lo,
+                            pos0=pos0, mode=2))
+    return out
+
+
+KVQ_CASES = _kvq_cases()
+
+
+@pytest.mark.parametrize("w", KVQ_CASES, ids=[_id(w) for w in KVQ_CASES])
+def test_sweep_kvq_case_matches_oracle(w):
+    check_kvq(w)
