@@ -456,10 +456,12 @@ prefill_quant_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc,
       C = mu;
     }
 
-    // S of tile i + 1 (i8 MFMA) after the weights of tile i: the wave reads
-    // its K operands, runs the vector work, then issues the MFMAs, and the
-    // other wave of the SIMD fills the gaps (about 1 % faster than
-    // interleaving each MFMA with a tenth of the vector work).
+    // S of tile i + 1 (i8 MFMA) and the weights of tile i. The groups below
+    // ask for the K operand reads, then the vector work, then the MFMAs; the
+    // compiler still sinks the weights past the closing barrier, where they
+    // run beside the P V MFMAs. Measured: about 1 % faster than one MFMA per
+    // tenth of the vector work; pinning the weights before the barrier was
+    // 1-2 % slower.
     s_mma((i + 1) & 1, nxt);
     i32x8 pb;
 #pragma unroll
