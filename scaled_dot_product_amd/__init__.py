@@ -152,8 +152,15 @@ def fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, *, causal=False, window_lo=0, pos
         _DTYPE[dtype]))
 
 
+def _same_device(ref: torch.Tensor, *named):
+    for t, name in named:
+        if t.device != ref.device:
+            raise AttnError(f"{name} must be on {ref.device}, like q")
+
+
 def _check_qkv(q, k, v):
     _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _same_device(q, (k, "k"), (v, "v"))
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
         raise AttnError("expected q [B,Hq,Nq,D] and k, v [B,Hkv,Nk,D]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
@@ -165,17 +172,27 @@ def _check_qkv(q, k, v):
     return B, Hq, Hkv, Nq, Nk, D
 
 
+def _workspace(q, workspace, need):
+    """Device pointer and byte length of the workspace (allocated when not
+    given): a given one must be a contiguous device tensor on q's device."""
+    if workspace is None:
+        if need <= 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    _same_device(q, (workspace, "workspace"))
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def _out_and_workspace(q, out, workspace, need):
     if out is None:
         out = torch.empty_like(q)
     else:
         _dev(out, "out")
+        _same_device(q, (out, "out"))
         if out.shape != q.shape or out.dtype != q.dtype:
             raise AttnError("out must match q's shape and dtype")
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace(q, workspace, need)
     return out, ws_ptr, ws_len
 
 
@@ -266,6 +283,7 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor):
     if Hq % Hkv != 0:
         raise AttnError("Hq must be a multiple of Hkv")
     _dev(q, "q"), _dev(k, "k")
+    _same_device(q, (k, "k"))
     qc = torch.empty(q.shape, dtype=torch.int8, device=q.device)
     kc = torch.empty(k.shape, dtype=torch.int8, device=k.device)
     qs = torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32, device=q.device)
@@ -329,6 +347,8 @@ def decode_kvq(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
     for t, name in ((q, "q"), (k_codes, "k_codes"), (k_scales, "k_scales"),
                     (v_codes, "v_codes"), (v_scales, "v_scales")):
         _dev(t, name)
+    _same_device(q, (k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                 (v_scales, "v_scales"))
     if q.dim() != 4 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape:
         raise AttnError("expected q [B,Hq,Nq,D] and k_codes, v_codes [B,Hkv,Nk,D]")
     if k_codes.dtype != torch.int8 or v_codes.dtype != torch.uint8:
@@ -343,19 +363,10 @@ def decode_kvq(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
             raise AttnError(f"{name} must be float32 of shape {sshape}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _dev(out, "out")
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise AttnError("out must match q's shape and dtype")
     dt = _DTYPE.get(q.dtype, -1)
     need = int(lib.attn_decode_kvq_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
                                                    int(window_lo), int(pos0), dt))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out, ws_ptr, ws_len = _out_and_workspace(q, out, workspace, need)
     st = lib.attn_decode_kvq(q.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(),
                              v_codes.data_ptr(), v_scales.data_ptr(), out.data_ptr(),
                              B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), int(window_lo),
@@ -414,6 +425,7 @@ def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal=Fal
         out = torch.empty_like(q)
     else:
         _dev(out, "out")
+        _same_device(q, (out, "out"))
         if out.shape != q.shape or out.dtype != q.dtype:
             raise AttnError("out must match q's shape and dtype")
     st = lib.attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -326,3 +326,31 @@ def test_decode_graph_replays_match_eager():
         e2 = sdpa.fwd(q, k, v, causal=True, pos0=w.pos0, scale=w.scale, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(e2, eager)
+
+
+def test_binding_rejects_host_workspace_and_outputs():
+    # a workspace or output in host memory would be written by the kernels
+    # through a host address: the binding refuses it before any launch
+    w = Workload("bind", 1, 2, 2, 64, 600, 128, torch.float16)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_qkv(w))
+    host_ws = torch.empty(1 << 20, dtype=torch.uint8)
+    for call in (lambda: sdpa.fwd(q, k, v, workspace=host_ws),
+                 lambda: sdpa.fwd_sliding(q, k, v, window=100, workspace=host_ws),
+                 lambda: sdpa.fwd_decode(q[:, :, :4].contiguous(), k, v, workspace=host_ws),
+                 lambda: sdpa.fwd(q, k, v, out=torch.empty(q.shape, dtype=q.dtype)),
+                 lambda: sdpa.fwd(q, k.cpu(), v)):
+        with pytest.raises(sdpa.AttnError):
+            call()
+    kc, ks = sdpa.quantize_qk(q, k)[2:]
+    vc, vs = sdpa.quantize_v(v)
+    with pytest.raises(sdpa.AttnError):
+        sdpa.decode_kvq(q[:, :, :4].contiguous(), kc, ks, vc, vs, workspace=host_ws)
+    with pytest.raises(sdpa.AttnError):
+        sdpa.decode_kvq(q[:, :, :4].contiguous(), kc, ks.cpu(), vc, vs)
+    # and a device workspace still works
+    ws = torch.empty(sdpa.fwd_workspace_bytes(1, 2, 2, 64, 600, 128, dtype=torch.float16) + 1,
+                     dtype=torch.uint8, device=dev)
+    out = sdpa.fwd(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
