@@ -682,9 +682,15 @@ hipError_t launch_t(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStrea
 // Eight waves (256 query rows) per workgroup halve the direct-load traffic
 // into LDS per flop, but one such workgroup fills a CU, so the last round of
 // workgroups runs the machine partly idle: they are used only for head dim
-// 128 when the grid is at least eight rounds of 256 workgroups.
+// 128 when the grid is at least eight rounds of 256 workgroups. Under a
+// per-row window of W keys a query tile of R rows covers W + R - 1 keys of
+// which each row uses W, so taller tiles compute more masked scores; below
+// 3072 keys the 128-row tiles win (measured: W = 1024 and 2048 run 8.6 % and
+// 2.3-3.7 % faster on four waves, 3072-6144 are even, 8192 and 16384 run
+// 0.6 % and 6.5 % slower).
 int prefill_waves(const FwdArgs& a) {
   const int64_t grid8 = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256);
+  if (a.window_w > 0 && a.window_w < 3072) return 4;
   return a.D == 128 && grid8 >= 8 * 256 ? 8 : 4;
 }
 

@@ -455,6 +455,13 @@ def test_dispatch_boundaries(lib):
     assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=128).waves == 8
     assert _plan(B=1, Hq=63, Hkv=63, Nq=8192, Nk=8192, D=128).waves == 4
     assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=64).waves == 4
+    # under a per-row window narrower than 3072 keys the 128-row tiles compute
+    # fewer masked scores: four waves even on a large grid
+    win = dict(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=128, causal=True)
+    assert _plan(window=2048, **win).waves == 4
+    assert _plan(window=3071, **win).waves == 4
+    assert _plan(window=3072, **win).waves == 8
+    assert _plan(window=2048, **win).workgroups == 64 * 8192 // 128
     # the MX mode, RoPE's extra pass and fp32 staging
     assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, mode=2).kernel == sdpa.KERNEL_PREFILL_MX
     assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=64, rope=True).pre_launches == 1

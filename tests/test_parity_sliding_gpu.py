@@ -54,9 +54,13 @@ def test_sliding_window_of_one_is_the_diagonal_value_bitwise():
     assert torch.equal(out, want)
 
 
-def test_sliding_eight_wave_grid_sampled():
-    # D = 128 and >= 2048 workgroups of 256 rows select the eight-wave kernel
-    w = Workload("sliding_w8", 1, 64, 64, 8192, 8192, 128, BF, causal=True, window_w=1024)
+@pytest.mark.parametrize("window, waves", [(4096, 8), (1024, 4)], ids=["eight-wave", "four-wave"])
+def test_sliding_large_grid_sampled(window, waves):
+    # D = 128 and >= 2048 workgroups of 256 rows select the eight-wave kernel,
+    # unless the per-row window is narrower than 3072 keys
+    w = Workload("sliding_grid", 1, 64, 64, 8192, 8192, 128, BF, causal=True, window_w=window)
+    p = sdpa.plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, causal=True, window=window, dtype=BF)
+    assert p.waves == waves
     q, k, v = make_qkv(w)
     rows = sample_rows(w, 192)
     check_workload(w, rows=rows, inputs=(q, k, v))
