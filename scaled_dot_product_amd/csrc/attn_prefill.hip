@@ -680,9 +680,15 @@ hipError_t launch_t(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStrea
 }  // namespace
 
 // Eight waves (256 query rows) per workgroup halve the direct-load traffic
-// into LDS per flop, but one such workgroup fills a CU, so the last round of
-// workgroups runs the machine partly idle: they are used only for head dim
-// 128 when the grid is at least eight rounds of 256 workgroups. Under a
+// into LDS per flop (about 5 % faster per full round at head dim 128), but
+// one such workgroup fills a CU, so a partial last round costs a whole round.
+// Four-wave workgroups run two to a CU; when their last round holds at most
+// 256 of them each runs alone on a CU, at 0.7-0.9 of a shared round's time.
+// So eight waves need at least one full round of 256 workgroups and either
+// no partial round, a last round more than half full, or eight rounds to
+// amortise it (measured: 256, 416, 512, 1000, 1024, 1184, 1536 and 2016
+// workgroups 4-9 % faster on eight waves; 300, 384, 640 and 1100, whose last
+// rounds are 17, 50, 50 and 30 % full, 9.4, 4.1, 7.0 and 0.6 % slower). Under a
 // per-row window of W keys a query tile of R rows covers W + R - 1 keys of
 // which each row uses W, so taller tiles compute more masked scores; below
 // 3072 keys the 128-row tiles win (measured: W = 1024 and 2048 run 8.6 % and
@@ -691,7 +697,9 @@ hipError_t launch_t(const FwdArgs& a, const PrefillSplit& pl, void* ws, hipStrea
 int prefill_waves(const FwdArgs& a) {
   const int64_t grid8 = (int64_t)a.B * a.Hq * ((a.Nq + 255) / 256);
   if (a.window_w > 0 && a.window_w < 3072) return 4;
-  return a.D == 128 && grid8 >= 8 * 256 ? 8 : 4;
+  if (a.D != 128 || grid8 < 256) return 4;
+  const int64_t tail = grid8 % 256;
+  return grid8 >= 8 * 256 || tail == 0 || tail > 128 ? 8 : 4;
 }
 
 // Parts per query tile: grids of at most 128 query tiles are split into 2

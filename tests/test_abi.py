@@ -451,9 +451,20 @@ def test_dispatch_boundaries(lib):
     p = _plan(B=65535, Hq=2, Hkv=1, Nq=1, Nk=4096, D=128, dtype=1)
     assert p.kernel == sdpa.KERNEL_DECODE
     assert sdpa.fwd_workspace_bytes(70000, 2, 1, 1, 4096, 128, dtype=f16) == 0
-    # eight-wave prefill only for head dim 128 and grids of >= 8 rounds of 256 workgroups
-    assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=128).waves == 8
-    assert _plan(B=1, Hq=63, Hkv=63, Nq=8192, Nk=8192, D=128).waves == 4
+    # eight-wave prefill only for head dim 128 and grids of at least one round of
+    # 256 workgroups whose last round is full, more than half full, or amortised
+    # over eight rounds
+    assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=128).waves == 8     # 2048
+    assert _plan(B=1, Hq=63, Hkv=63, Nq=8192, Nk=8192, D=128).waves == 8     # 2016: 8 rounds - 32
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=32768, Nk=4096, D=128).waves == 8      # 256: one round
+    assert _plan(B=1, Hq=1, Hkv=1, Nq=65280, Nk=4096, D=128).waves == 4      # 255
+    assert _plan(B=1, Hq=20, Hkv=20, Nq=12800, Nk=4096, D=128).waves == 8    # 1000: tail 232
+    assert _plan(B=1, Hq=11, Hkv=11, Nq=25600, Nk=4096, D=128).waves == 4    # 1100: tail 76
+    assert _plan(B=1, Hq=4, Hkv=4, Nq=19200, Nk=4096, D=128).waves == 4      # 300: tail 44
+    assert _plan(B=1, Hq=3, Hkv=3, Nq=32768, Nk=4096, D=128).waves == 4      # 384: tail 128
+    assert _plan(B=1, Hq=13, Hkv=13, Nq=8192, Nk=4096, D=128).waves == 8     # 416: tail 160
+    assert _plan(B=1, Hq=1, Hkv=1, Nq=98560, Nk=4096, D=128).waves == 8      # 385: tail 129
+    assert _plan(B=2, Hq=1, Hkv=1, Nq=33024, Nk=4096, D=128).waves == 4      # 258: tail 2
     assert _plan(B=1, Hq=64, Hkv=64, Nq=8192, Nk=8192, D=64).waves == 4
     # under a per-row window narrower than 3072 keys the 128-row tiles compute
     # fewer masked scores: four waves even on a large grid
