@@ -15,6 +15,8 @@ the definitions and the passages they follow):
 * :func:`attn_kvq` — exact attention over a quantised KV cache (codes + scales).
 * :func:`quant_mx` — OCP MX FP8 blocks (32 E4M3 elements, one E8M0 scale).
 * :func:`attn_mx` — exact attention on the MX variant's inputs (INT8 Q, K; MX V).
+* :func:`quant_mx4`, :func:`e2m1_encode`, :func:`e2m1_decode` — OCP MX FP4 blocks.
+* :func:`attn_mxd` — the diagonal-tiled mixed MXFP8 / MXFP4 variant, weights rounded.
 * :func:`rope_freqs`, :func:`rope_apply`, :func:`attn_rope` — rotary position
   embedding (plain, NTK, YaRN) and attention on rotated Q, K.
 
@@ -73,6 +75,15 @@ def _load():
         lib.oracle_quant_mx.restype = i
         lib.oracle_attn_mx.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, d, vp, i64, vp, i]
         lib.oracle_attn_mx.restype = i
+        lib.oracle_quant_mx4.argtypes = [vp, i, i64, i, i, i, vp, vp]
+        lib.oracle_quant_mx4.restype = i
+        lib.oracle_attn_mxd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, d, vp, i64,
+                                        vp, i]
+        lib.oracle_attn_mxd.restype = i
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_decode.restype = ctypes.c_float
         lib.oracle_rope_freqs.argtypes = [i, i, d, d, i, d, d, vp, vp]
         lib.oracle_rope_freqs.restype = i
         lib.oracle_rope_apply.argtypes = [vp, i, i64, i, i, i, i, vp, vp]
@@ -240,6 +251,55 @@ def attn_mx(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, rows=None, nth
     if rc != 0:
         raise ValueError("oracle_attn_mx rejected the arguments")
     return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+def quant_mx4(x, axis=0):
+    """MX FP4 codes (one uint8 per element holding the 4-bit E2M1 code, x's
+    layout) and E8M0 scale bytes, laid out as quant_mx's."""
+    x = _cpu(x)
+    *lead, N, D = x.shape
+    BH = int(np.prod(lead)) if lead else 1
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    sshape = tuple(lead) + ((N, D // 32) if axis == 0 else ((N + 31) // 32, D))
+    scales = np.zeros(sshape, dtype=np.uint8)
+    rc = _load().oracle_quant_mx4(x.data_ptr(), DTYPE_CODE[x.dtype], BH, N, D, int(axis),
+                                  codes.ctypes.data, scales.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_quant_mx4 rejected the arguments")
+    return codes, scales
+
+
+def attn_mxd(q, k, v, *, scale, causal=False, window_lo=0, pos0=0, window_w=0, rows=None,
+             nthreads=None):
+    """The diagonal-tiled mixed MX variant in fp64: Q and K through their
+    per-64-token INT8 blocks; per row, the weights of each 32-key block and V
+    in MXFP8 on the row's diagonal key tiles and in MXFP4 elsewhere, rounded as
+    the variant rounds them. Same conventions as attn()."""
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if rows is None:
+        nrows, rows_arr = B * Hq * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_attn_mxd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPE_CODE[q.dtype],
+        B, Hq, Hkv, Nq, Nk, D, int(causal), int(window_lo), int(pos0), int(window_w),
+        float(scale), None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        out.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_mxd rejected the arguments")
+    return out.reshape(B, Hq, Nq, D) if rows is None else out
+
+
+def e2m1_encode(y: float) -> int:
+    return int(_load().oracle_e2m1_encode(float(y)))
+
+
+def e2m1_decode(code: int) -> float:
+    return float(_load().oracle_e2m1_decode(int(code)))
 
 
 ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2

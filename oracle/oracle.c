@@ -35,6 +35,12 @@
  *                       sharing one power-of-two (E8M0) scale, along D or N.
  *   oracle_attn_mx      exact attention on the MX variant's inputs: INT8
  *                       Q, K blocks and V in MX blocks along the keys.
+ *   oracle_e2m1_encode  / oracle_e2m1_decode: OCP FP4 E2M1.
+ *   oracle_quant_mx4    OCP MX FP4 blocks: 32 E2M1 elements, one E8M0 scale.
+ *   oracle_attn_mxd     the diagonal-tiled mixed MX variant: INT8 Q, K; per
+ *                       row, P and V in MXFP8 on diagonal key tiles and in
+ *                       MXFP4 elsewhere, every weight rounded as the variant
+ *                       rounds it.
  *   oracle_rope_freqs   rotary frequencies: plain, NTK-aware, YaRN.
  *   oracle_rope_apply   the rotation of Q or K rows at their positions.
  *   oracle_attn_rope    exact attention on rotated Q and K.
@@ -122,12 +128,17 @@ typedef struct {
   const double* khat;
   const double* vhat;
   int quant_p;           /* 1: pass each weight through E4M3 at scale 448 */
+  const double* vhat4;   /* non-NULL: the diagonal-tiled MX emulation, V through
+                            MXFP4 off the diagonal (vhat: MXFP8 on it) */
   int64_t next;          /* work counter */
   pthread_mutex_t mu;
 } attn_job;
 
 uint8_t oracle_e4m3_encode(float y);
 float oracle_e4m3_decode(uint8_t code);
+uint8_t oracle_e2m1_encode(float y);
+float oracle_e2m1_decode(uint8_t code);
+static void mxd_row(const attn_job* J, int i, int64_t kvoff, const double* s, double m, double* o);
 
 /* Key j is visible to query row i. */
 static int visible(const attn_job* J, int i, int j) {
@@ -176,6 +187,10 @@ static void attn_one_row(const attn_job* J, int64_t slot, double* s) {
     for (int j = 0; j < Nk; ++j) J->weights[slot * Nk + j] = 0.0;
   if (!any) {
     if (J->lse) J->lse[slot] = -INFINITY;
+    return;
+  }
+  if (J->vhat4) {
+    mxd_row(J, i, kvoff, s, m, o);
     return;
   }
   double l = 0.0;
@@ -540,6 +555,216 @@ int oracle_attn_mx(const void* q, const void* k, const void* v, int dtype,
     rc = run_attn(&J, nthreads);
   }
   free(qh); free(kh); free(vh);
+  return rc;
+}
+
+/* ---------------------------------------------------- MX FP4 blocks -- */
+
+/*
+ * The diagonal-tiled mixed-precision MX variant ("Diagonal-Tiled
+ * Mixed-Precision Attention" in "Transformers Get a Turbo Boost with
+ * Mixed-Precision Magic", section "The DMA breakthrough": two low-bit MXFP
+ * computations combined at the tiling level, the diagonal treated apart; the
+ * FP4 rows of the table in section 1 of "Attention kernels on a home RTX
+ * 5080"). The pages give no arithmetic; the element format is OCP FP4 E2M1
+ * (OCP Microscaling Formats v1.0): 1 sign bit, 2 exponent bits biased by 1,
+ * 1 mantissa bit, exponent field 0 subnormal; magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinities or NaN.
+ */
+float oracle_e2m1_decode(uint8_t code) {
+  int sign = (code >> 3) & 1;
+  int e = (code >> 1) & 3;
+  int m = code & 1;
+  float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return sign ? -v : v;
+}
+
+/*
+ * Encode to E2M1 by brute force: the nearest of the 8 magnitudes (codes
+ * 0..7), ties to the even code (round-to-nearest-even); magnitudes above 6
+ * saturate to 6 (callers clamp first). The sign is bit 3. NaN gives 0.
+ */
+uint8_t oracle_e2m1_encode(float y) {
+  if (isnan(y)) return 0;
+  uint8_t sign = signbit(y) ? 0x8 : 0x0;
+  double a = fabs((double)y);
+  if (a > 6.0) a = 6.0;   /* infinities included */
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 7; ++c) {
+    double err = fabs((double)oracle_e2m1_decode((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/*
+ * OCP MX FP4 blocks: as oracle_quant_mx, with E2M1 elements. Per block:
+ * amax == 0 gives scale byte 0 and zero codes; otherwise e = floor(log2 amax)
+ * - 2 (2: the exponent of the largest power of two in E2M1, 4), clamped to
+ * [-127, 127], and code = E2M1(clamp(x * 2^-e, -6, 6)) rounded to nearest
+ * even. codes: one byte per element (the 4-bit code in bits 0..3), same
+ * layout as x; scales as oracle_quant_mx.
+ */
+int oracle_quant_mx4(const void* x, int dtype, int64_t BH, int N, int D, int axis,
+                     uint8_t* codes, uint8_t* scales) {
+  if (BH < 1 || N < 1 || D < 1) return -1;
+  if (axis == 0 && D % 32 != 0) return -1;
+  if (axis != 0 && axis != 1) return -1;
+  int nb = axis == 0 ? D / 32 : (N + 31) / 32;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    int outer = axis == 0 ? N : nb;
+    int inner = axis == 0 ? nb : D;
+    for (int o = 0; o < outer; ++o) {
+      for (int in = 0; in < inner; ++in) {
+        int64_t idx[32];
+        int cnt = 0;
+        for (int j = 0; j < 32; ++j) {
+          int tok = axis == 0 ? o : 32 * o + j;
+          int ch = axis == 0 ? 32 * in + j : in;
+          if (tok >= N) break;
+          idx[cnt++] = (bh * N + tok) * (int64_t)D + ch;
+        }
+        float amax = 0.0f;
+        for (int j = 0; j < cnt; ++j) {
+          float a = fabsf(load_elem_f(x, dtype, idx[j]));
+          if (a > amax) amax = a;
+        }
+        int64_t sidx = (bh * outer + o) * (int64_t)inner + in;
+        if (amax == 0.0f) {
+          scales[sidx] = 0;
+          for (int j = 0; j < cnt; ++j) codes[idx[j]] = 0;
+          continue;
+        }
+        int ex;
+        frexpf(amax, &ex);                 /* amax = m * 2^ex, m in [0.5, 1) */
+        int e = (ex - 1) - 2;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+        scales[sidx] = (uint8_t)(e + 127);
+        for (int j = 0; j < cnt; ++j) {
+          float y = ldexpf(load_elem_f(x, dtype, idx[j]), -e);
+          if (y > 6.0f) y = 6.0f;
+          if (y < -6.0f) y = -6.0f;
+          codes[idx[j]] = oracle_e2m1_encode(y);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* MX FP4 dequantisation into doubles, axis 1 (blocks of 32 tokens). */
+static int dequant_mx4(const void* x, int dtype, int64_t BH, int N, int D, double* out) {
+  int64_t n = BH * (int64_t)N * D;
+  int64_t ns = BH * (int64_t)((N + 31) / 32) * D;
+  uint8_t* c = (uint8_t*)malloc((size_t)n);
+  uint8_t* s = (uint8_t*)malloc((size_t)ns);
+  if (!c || !s || oracle_quant_mx4(x, dtype, BH, N, D, 1, c, s) != 0) { free(c); free(s); return -1; }
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t bh = e / ((int64_t)N * D);
+    int tok = (int)((e / D) % N), ch = (int)(e % D);
+    int64_t si = (bh * ((N + 31) / 32) + tok / 32) * (int64_t)D + ch;
+    out[e] = ldexp((double)oracle_e2m1_decode(c[e]), (int)s[si] - 127);
+  }
+  free(c); free(s);
+  return 0;
+}
+
+/*
+ * Key tile t (keys 64 t .. 64 t + 63) is on the diagonal of query row i when
+ * it holds the position of one of the rows of i's 32-row block r = i / 32,
+ * i.e. [64 t, 64 t + 63] meets [pos0 + 32 r, pos0 + 32 r + 31] (row i sits
+ * at position pos0 + i).
+ */
+static int mxd_diagonal(int pos0, int i, int j) {
+  int64_t r0 = (int64_t)pos0 + 32 * (int64_t)(i / 32);
+  int64_t k0 = 64 * (int64_t)(j / 64);
+  return k0 <= r0 + 31 && k0 + 63 >= r0;
+}
+
+/*
+ * One row of the diagonal-tiled MX emulation, given its scores s (natural
+ * units, visible keys only) and their maximum m. The weights of each block of
+ * 32 consecutive keys (keys 32 b .. 32 b + 31) are one MX block of the row:
+ * with x_b the block's largest score in log2 units (scale * log2 e * q.k),
+ * its scale is 2^E, E = floor(x_b) - 7 on diagonal tiles (E4M3 elements, all
+ * below 256, none saturated) and E = floor(x_b) - 2 elsewhere (E2M1, the OCP
+ * rule: elements clamped to 6); each weight 2^(x_j - E) is rounded to the
+ * element format. V is MXFP8 on diagonal tiles and MXFP4 elsewhere (blocks of
+ * 32 keys of one channel). O = sum_j P^_j V^_j / sum_j P^_j. Every quantity is
+ * taken relative to the integer floor(m log2 e), which changes no rounding.
+ */
+static void mxd_row(const attn_job* J, int i, int64_t kvoff, const double* s, double m, double* o) {
+  const double L2E = 1.4426950408889634;
+  int D = J->D, Nk = J->Nk;
+  double M = floor(m * L2E);
+  double l = 0.0;
+  for (int b0 = 0; b0 < Nk; b0 += 32) {
+    int b1 = b0 + 32 < Nk ? b0 + 32 : Nk;
+    double xb = -INFINITY;
+    for (int j = b0; j < b1; ++j)
+      if (visible(J, i, j) && s[j] * L2E - M > xb) xb = s[j] * L2E - M;
+    if (xb == -INFINITY) continue;
+    int diag = mxd_diagonal(J->pos0, i, b0);   /* a 32-key block lies in one tile */
+    double E = floor(xb) - (diag ? 7.0 : 2.0);
+    for (int j = b0; j < b1; ++j) {
+      if (!visible(J, i, j)) continue;
+      double w = exp2(s[j] * L2E - M - E);
+      double pq;
+      if (diag) {
+        pq = (double)oracle_e4m3_decode(oracle_e4m3_encode((float)w));
+      } else {
+        float y = w > 6.0 ? 6.0f : (float)w;
+        pq = (double)oracle_e2m1_decode(oracle_e2m1_encode(y));
+      }
+      pq = ldexp(pq, (int)E);
+      l += pq;
+      const double* vh = diag ? J->vhat : J->vhat4;
+      for (int d = 0; d < D; ++d) o[d] += pq * vh[kvoff + (int64_t)j * D + d];
+    }
+  }
+  for (int d = 0; d < D; ++d) o[d] = l > 0.0 ? o[d] / l : 0.0;
+}
+
+/*
+ * The diagonal-tiled MX variant's reference (arguments of oracle_attn_mx,
+ * plus the per-row window): Q and K through their per-64-token INT8 blocks,
+ * then per row the weights and V as mxd_row describes.
+ */
+int oracle_attn_mxd(const void* q, const void* k, const void* v, int dtype,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                    int causal, int window_lo, int pos0, int window_w, double scale,
+                    const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, D) || D % 32 != 0 || window_w < 0) return -1;
+  if (dtype < OR_F32 || dtype > OR_BF16) return -1;
+  int64_t nq = (int64_t)B * Hq * Nq * D, nk = (int64_t)B * Hkv * Nk * D;
+  double* qh = (double*)malloc(sizeof(double) * (size_t)nq);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* vh = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* vh4 = (double*)malloc(sizeof(double) * (size_t)nk);
+  int rc = -1;
+  if (qh && kh && vh && vh4 &&
+      dequant_int8(q, dtype, (int64_t)B * Hq, Nq, D, qh) == 0 &&
+      dequant_int8(k, dtype, (int64_t)B * Hkv, Nk, D, kh) == 0 &&
+      dequant_mx(v, dtype, (int64_t)B * Hkv, Nk, D, 1, vh) == 0 &&
+      dequant_mx4(v, dtype, (int64_t)B * Hkv, Nk, D, vh4) == 0) {
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.D = D;
+    J.causal = causal; J.window_lo = window_lo; J.pos0 = pos0; J.window_w = window_w;
+    J.scale = scale;
+    J.rows = rows;
+    J.nrows = rows ? nrows : (int64_t)B * Hq * Nq;
+    J.out = out;
+    J.qhat = qh; J.khat = kh; J.vhat = vh; J.vhat4 = vh4;
+    rc = run_attn(&J, nthreads);
+  }
+  free(qh); free(kh); free(vh); free(vh4);
   return rc;
 }
 
