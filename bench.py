@@ -41,6 +41,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 / int8 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 MFMA
+# half INT8 (Q K^T), half FP4 (P V): 1 / (0.5 / 5000 + 0.5 / 10100)
+PEAK_INT8_FP4_TOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_FP4_TFLOPS)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "attention fwd TFLOPS (%bf16 MFMA peak) at 40×32760×128; decode µs + HBM GB/s"
 # Context only (another machine, not a baseline): PyTorch SDPA takes 511 ms on
@@ -524,6 +527,16 @@ def run_extra(part):
                        "tops": round(wm.flops() / (ms_m * 1e-3) / 1e12, 2),
                        "frac_of_fp8_peak": round(wm.flops() / (ms_m * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
         log(f"mx: {ms_m:.3f} ms/call incl. preparation")
+    elif part == "mxd":
+        # the diagonal-tiled mode: half of the work (Q K^T) on the INT8 matrix
+        # cores (5.0 POP/s), the other half (P V) almost all on FP4 ones (10.1
+        # PFLOP/s): a combined peak of 1 / (0.5 / 5.0 + 0.5 / 10.1) = 6.69 POP/s
+        wd = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_mxd_32760", mode=3)
+        ms_d = bench_prefill(wd, 10, 2)
+        tops = wd.flops() / (ms_d * 1e-3) / 1e12
+        extra["mxd"] = {"workload": wd.name, "ms_per_call": round(ms_d, 4), "tops": round(tops, 2),
+                        "frac_of_int8_fp4_peak": round(tops / PEAK_INT8_FP4_TOPS, 4)}
+        log(f"mxd: {ms_d:.3f} ms/call incl. preparation")
     elif part == "rope":
         import torch
         import scaled_dot_product_amd as sdpa
@@ -687,6 +700,9 @@ def ab_part(part):
     if part == "mx":
         w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_mx_32760", mode=2)
         return "ms", lambda: bench_prefill(w, 6, 1)
+    if part == "mxd":
+        w = WORKLOADS["video_dit_bf16_32760"].variant(name="video_dit_mxd_32760", mode=3)
+        return "ms", lambda: bench_prefill(w, 6, 1)
     if part in ("decode", "decode_window1000"):
         w = WORKLOADS["gqa_decode_f16_4096"].variant(window_lo=0 if part == "decode" else 1000)
         return "us", lambda: bench_decode(w, reps=20)[0]
@@ -747,7 +763,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="time the headline step only")
     ap.add_argument("--only", choices=["decode", "decode_kvq", "decode_cold", "decode_kvq_cold",
                                        "decode_chunks", "valu",
-                                       "quant", "mx", "rope", "causal", "sliding", "sdxl", "copy",
+                                       "quant", "mx", "mxd", "rope", "causal", "sliding", "sdxl",
+                                       "copy",
                                        "floor"],
                     help="time one secondary workload only (for kernel profiles); "
                          "'copy' runs a plain 1 GiB device copy, the reference for "
@@ -797,8 +814,8 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        for part in ("quant", "mx", "rope", "causal", "sliding", "sdxl", "decode", "decode_kvq",
-                     "floor"):
+        for part in ("quant", "mx", "mxd", "rope", "causal", "sliding", "sdxl", "decode",
+                     "decode_kvq", "floor"):
             extra.update(run_extra(part))
 
     peaks = measured_peaks()

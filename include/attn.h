@@ -59,7 +59,7 @@ typedef enum {
                           scales ("SageAttention 2 INT8 QK . FP8 PV" row of
                           the table in section 1 of "Attention kernels on a
                           home RTX 5080"); bf16/f16 inputs only */
-  ATTN_MODE_MX = 2     /* INT8 Q K^T as in ATTN_MODE_QUANT, and P V in OCP
+  ATTN_MODE_MX = 2,    /* INT8 Q K^T as in ATTN_MODE_QUANT, and P V in OCP
                           MX FP8 blocks: V in blocks of 32 keys of each
                           channel (attn_quantize_mx, axis 1), the softmax
                           weights in blocks of 32 keys of each row, both E8M0
@@ -67,6 +67,25 @@ typedef enum {
                           (the per-block-scaled low-precision kernels of that
                           table, MXFP as in "Transformers Get a Turbo Boost
                           with Mixed-Precision Magic"); bf16/f16 inputs only */
+  ATTN_MODE_MXD = 3    /* the diagonal-tiled mixed MX variant ("Diagonal-
+                          Tiled Mixed-Precision Attention", section "The DMA
+                          breakthrough" of "Transformers Get a Turbo Boost
+                          with Mixed-Precision Magic"; FP4 with per-block
+                          scales in the table of section 1 of "Attention
+                          kernels on a home RTX 5080"). INT8 Q K^T as above.
+                          The map is tiled into 32-row blocks (rows 32 r ..
+                          32 r + 31) and 64-key tiles; a tile holding the
+                          position of one of its block's rows (key tile t
+                          meets [pos0 + 32 r, pos0 + 32 r + 31]) is diagonal
+                          and runs P V as ATTN_MODE_MX (MXFP8); every other
+                          tile runs it in OCP MXFP4 (E2M1 elements): V in
+                          blocks of 32 keys of each channel (attn_quantize_
+                          mx4, axis 1), the weights of each 32-key block of a
+                          row with scale 2^E, E = floor(log2 block max) - 2,
+                          clamped to 6 and rounded to nearest even, on the
+                          FP4 matrix cores at about twice the FP8 rate. Far
+                          less precise (about 18 % relative error against
+                          exact attention on normal inputs); bf16/f16 only */
 } attn_mode;
 
 /*
@@ -256,6 +275,27 @@ int attn_quantize_mx(const void* x, uint8_t* codes, uint8_t* scales, int B, int 
                      int D, int axis, int dtype, void* stream);
 
 /*
+ * attn_quantize_mx4 — OCP Microscaling (MX) FP4 blocks of ATTN_MODE_MXD's
+ * off-diagonal tiles (OCP Microscaling Formats v1.0; the pages name FP4 and
+ * MXFP without a format): 32 elements share one scale 2^e stored as an E8M0
+ * byte e + 127, and each element is an E2M1 code (sign, 2 exponent bits
+ * biased by 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6). Per
+ * block, in fp32: amax == 0 gives scale byte 0 and zero codes; otherwise e =
+ * floor(log2 amax) - 2 clamped to [-127, 127] and code = E2M1(clamp(x * 2^-e,
+ * -6, 6)) rounded to nearest even.
+ *
+ *   x        device [B][H][N][D], bf16/f16 (`dtype`); D = 64 or 128.
+ *   codes    device uint8 [B][H][N][D / 2]: byte c of a row holds channel 2c
+ *            in bits 0..3 and channel 2c + 1 in bits 4..7.
+ *   scales   device uint8, as attn_quantize_mx: axis 0 [B][H][N][D/32],
+ *            axis 1 [B][H][ceil(N/32)][D].
+ * Codes and scales are bit-exact with the CPU oracle's definition. Errors as
+ * attn_quantize_mx; nothing is allocated.
+ */
+int attn_quantize_mx4(const void* x, uint8_t* codes, uint8_t* scales, int B, int H, int N,
+                      int D, int axis, int dtype, void* stream);
+
+/*
  * attn_decode_kvq — decode over a quantised KV cache: the split-KV decode of
  * attn_fwd reading K and V as the per-block codes that attn_quantize_qk (its
  * K half) and attn_quantize_v write, at half the bytes of a 16-bit cache.
@@ -344,7 +384,8 @@ typedef enum {
   ATTN_KERNEL_PREFILL = 1,        /* exact-mode prefill (bf16/f16 matrix cores) */
   ATTN_KERNEL_DECODE = 2,         /* exact-mode split-KV decode, fused merge */
   ATTN_KERNEL_PREFILL_QUANT = 3,  /* INT8 Q K^T, FP8 P V */
-  ATTN_KERNEL_PREFILL_MX = 4      /* INT8 Q K^T, MX FP8 P V */
+  ATTN_KERNEL_PREFILL_MX = 4,     /* INT8 Q K^T, MX FP8 P V */
+  ATTN_KERNEL_PREFILL_MXD = 5     /* INT8 Q K^T, MX FP8 / FP4 P V by tile */
 } attn_kernel;
 
 typedef struct {

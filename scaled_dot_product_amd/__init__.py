@@ -19,21 +19,24 @@ import torch
 __all__ = ["fwd", "fwd_workspace_bytes", "fwd_sliding", "fwd_sliding_workspace_bytes",
            "fwd_rope", "fwd_rope_workspace_bytes", "Rope", "ROPE_HALF", "ROPE_INTERLEAVED",
            "ROPE_PLAIN", "ROPE_NTK", "ROPE_YARN",
-           "quantize_qk", "quantize_v", "quantize_mx", "decode_kvq",
+           "quantize_qk", "quantize_v", "quantize_mx", "quantize_mx4", "decode_kvq",
            "decode_kvq_workspace_bytes", "fwd_decode", "fwd_decode_workspace_bytes", "plan",
            "Plan", "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_PREFILL_QUANT", "KERNEL_PREFILL_MX",
+           "KERNEL_PREFILL_MXD",
            "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "load_library", "open_library", "using",
-           "MODE_EXACT", "MODE_QUANT", "MODE_MX", "AttnError", "LIB_PATH"]
+           "MODE_EXACT", "MODE_QUANT", "MODE_MX", "MODE_MXD", "AttnError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 MODE_EXACT = 0
 MODE_QUANT = 1
 MODE_MX = 2
+MODE_MXD = 3      # diagonal-tiled mixed MXFP8 / MXFP4 (ATTN_MODE_MXD)
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 ROPE_PLAIN, ROPE_NTK, ROPE_YARN = 0, 1, 2
 KERNEL_PREFILL, KERNEL_DECODE, KERNEL_PREFILL_QUANT, KERNEL_PREFILL_MX = 1, 2, 3, 4
+KERNEL_PREFILL_MXD = 5
 NOALLOC_SCRATCH_BYTES = 16 << 20      # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
 
 
@@ -96,6 +99,8 @@ def open_library(path: str):
     lib.attn_quantize_v.restype = i
     lib.attn_quantize_mx.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
     lib.attn_quantize_mx.restype = i
+    lib.attn_quantize_mx4.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.attn_quantize_mx4.restype = i
     lib.attn_decode_kvq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
                                      vp, sz, vp]
     lib.attn_decode_kvq.restype = i
@@ -325,6 +330,24 @@ def quantize_mx(x: torch.Tensor, axis: int = 0):
     st = lib.attn_quantize_mx(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, D,
                               int(axis), _DTYPE.get(x.dtype, -1), _stream_handle(x))
     _check(st, "attn_quantize_mx")
+    return codes, scales
+
+
+def quantize_mx4(x: torch.Tensor, axis: int = 0):
+    """OCP MX FP4 codes (uint8 [B, H, N, D/2]: channel 2c in bits 0..3 of byte
+    c, 2c + 1 in bits 4..7) and E8M0 scale bytes (uint8, laid out as
+    quantize_mx's) of x [B, H, N, D] (bf16/f16)."""
+    lib = load_library()
+    _dev(x, "x")
+    if x.dim() != 4:
+        raise AttnError("expected x [B,H,N,D]")
+    B, H, N, D = x.shape
+    codes = torch.empty((B, H, N, D // 2), dtype=torch.uint8, device=x.device)
+    sshape = (B, H, N, D // 32) if axis == 0 else (B, H, (N + 31) // 32, D)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    st = lib.attn_quantize_mx4(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, D,
+                               int(axis), _DTYPE.get(x.dtype, -1), _stream_handle(x))
+    _check(st, "attn_quantize_mx4")
     return codes, scales
 
 

@@ -42,7 +42,8 @@ int check_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int win
   if (st != ATTN_OK) return st;
   if (window_lo < 0 || pos0 < 0) return ATTN_E_INVALID;
   if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_E_INVALID;
-  if (mode != ATTN_MODE_EXACT && mode != ATTN_MODE_QUANT && mode != ATTN_MODE_MX)
+  if (mode != ATTN_MODE_EXACT && mode != ATTN_MODE_QUANT && mode != ATTN_MODE_MX &&
+      mode != ATTN_MODE_MXD)
     return ATTN_E_UNSUPPORTED;
   if (mode != ATTN_MODE_EXACT && dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
   return ATTN_OK;
@@ -82,6 +83,7 @@ FwdArgs make_args(const void* q, const void* k, const void* v, void* o, int B, i
 struct Layout {
   size_t bf16_q = 0, bf16_k = 0, bf16_v = 0;       // fp32 inputs rounded to bf16
   size_t qc = 0, qs = 0, kc = 0, ks = 0, vc = 0, vs = 0;  // quantised mode
+  size_t v4c = 0, v4s = 0, part = 0;                // MXFP4 V, row partials (diagonal-tiled)
   size_t dec = 0;                                  // decode partials
   size_t rk = 0;                                   // rotated K (exact mode with RoPE)
   size_t spl = 0;                                  // split-prefill counters and partials
@@ -100,7 +102,7 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1,
   size_t off = 0;
   const size_t nq = (size_t)a.B * a.Hq * a.Nq * a.D;
   const size_t nk = (size_t)a.B * a.Hkv * a.Nk * a.D;
-  if (mode == ATTN_MODE_MX) {
+  if (mode == ATTN_MODE_MX || mode == ATTN_MODE_MXD) {
     const size_t tiles = (size_t)(a.Nk + 63) / 64;
     L.qc = off; off = round_up(off + nq);
     L.qs = off; off = round_up(off + (size_t)a.B * a.Hq * ((a.Nq + 63) / 64) * 4);
@@ -108,6 +110,11 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1,
     L.ks = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 4);
     L.vc = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 64 * a.D);
     L.vs = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 2 * a.D);
+    if (mode == ATTN_MODE_MXD) {
+      L.v4c = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 32 * a.D);
+      L.v4s = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 2 * a.D);
+      L.part = off; off = round_up(off + (size_t)a.B * a.Hq * a.Nq * (a.D + 4) * 4);
+    }
     L.total = off;
     return L;
   }
@@ -208,8 +215,9 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
   hipError_t e = hipSuccess;
 
   const RopeArgs* rope = a.rope.on ? &a.rope : nullptr;   // fused into the INT8 quantiser
-  if (mode == ATTN_MODE_MX) {
+  if (mode == ATTN_MODE_MX || mode == ATTN_MODE_MXD) {
     const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+    const bool dg = mode == ATTN_MODE_MXD;
     e = launch_quant_int8(q, elem, (int64_t)B * Hq, Nq, D, (int8_t*)(ws + L.qc),
                           (float*)(ws + L.qs), s, rope, a.pos0);
     if (e == hipSuccess)
@@ -218,10 +226,16 @@ int fwd_dispatch(FwdArgs a, int mode, int dtype, void* workspace, size_t workspa
     if (e == hipSuccess)
       e = launch_quant_mx(v, elem, (int64_t)B * Hkv, Nk, D, 1, 1, 0, (uint8_t*)(ws + L.vc),
                           (uint8_t*)(ws + L.vs), s);
+    if (e == hipSuccess && dg)
+      e = launch_quant_mx(v, elem, (int64_t)B * Hkv, Nk, D, 1, 1, 0, (uint8_t*)(ws + L.v4c),
+                          (uint8_t*)(ws + L.v4s), s, true);
     if (e == hipSuccess)
       e = launch_prefill_mx(a, (const int8_t*)(ws + L.qc), (const float*)(ws + L.qs),
                             (const int8_t*)(ws + L.kc), (const float*)(ws + L.ks),
-                            (const uint8_t*)(ws + L.vc), (const uint8_t*)(ws + L.vs), elem, s);
+                            (const uint8_t*)(ws + L.vc), (const uint8_t*)(ws + L.vs),
+                            dg ? (const uint8_t*)(ws + L.v4c) : nullptr,
+                            dg ? (const uint8_t*)(ws + L.v4s) : nullptr,
+                            dg ? (float*)(ws + L.part) : nullptr, elem, s);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   }
   if (mode == ATTN_MODE_QUANT) {
@@ -411,6 +425,20 @@ int attn_quantize_mx(const void* x, uint8_t* codes, uint8_t* scales, int B, int 
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+int attn_quantize_mx4(const void* x, uint8_t* codes, uint8_t* scales, int B, int H, int N, int D,
+                      int axis, int dtype, void* stream) {
+  int st = check_shape(B, H, H, N, 1, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_DT_F32) return ATTN_E_UNSUPPORTED;
+  if (axis != 0 && axis != 1) return ATTN_E_INVALID;
+  if (!x || !codes || !scales) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(codes)) return ATTN_E_INVALID;
+  const int elem = dtype == ATTN_DT_BF16 ? 2 : 1;
+  const hipError_t e = launch_quant_mx(x, elem, (int64_t)B * H, N, D, axis, 0, N, codes, scales,
+                                       (hipStream_t)stream, true);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
 size_t attn_decode_kvq_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D,
                                        int causal, int window_lo, int pos0, int dtype) {
   if (check_kvq(B, Hq, Hkv, Nq, Nk, D, window_lo, pos0, 1.0f, dtype) != ATTN_OK) return 0;
@@ -479,12 +507,15 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, int
   attn_plan p;
   p.workspace_bytes = L.total;
   p.splits = 1;
-  if (mode == ATTN_MODE_QUANT || mode == ATTN_MODE_MX) {
-    p.kernel = mode == ATTN_MODE_QUANT ? ATTN_KERNEL_PREFILL_QUANT : ATTN_KERNEL_PREFILL_MX;
+  if (mode == ATTN_MODE_QUANT || mode == ATTN_MODE_MX || mode == ATTN_MODE_MXD) {
+    p.kernel = mode == ATTN_MODE_QUANT ? ATTN_KERNEL_PREFILL_QUANT
+               : mode == ATTN_MODE_MX  ? ATTN_KERNEL_PREFILL_MX
+                                       : ATTN_KERNEL_PREFILL_MXD;
     p.waves = 4;
     p.rows = 128;
     p.workgroups = (long long)B * Hq * ((Nq + 127) / 128);
-    p.pre_launches = 3;   // INT8 Q, INT8 K (rotated there with RoPE), V codes
+    // INT8 Q, INT8 K (rotated there with RoPE), V codes (and MXFP4 V codes)
+    p.pre_launches = mode == ATTN_MODE_MXD ? 4 : 3;
   } else if (L.decode) {
     p.kernel = ATTN_KERNEL_DECODE;
     p.waves = L.plan.waves;

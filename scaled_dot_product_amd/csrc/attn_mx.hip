@@ -39,9 +39,29 @@ __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d,
   return (uint32_t)pk;
 }
 
+// The FP4 (E2M1) block exponent of the OCP rule: floor(log2 amax) - 2, 2
+// being the exponent of the largest power of two in E2M1 (4).
+__device__ __forceinline__ int mx4_exp(float amax) {
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  return min(max(ex - 1 - 2, -127), 127);
+}
+
+// Eight E2M1 codes of x * 2^-e (clamped to +-6), nibble i = element i.
+__device__ __forceinline__ uint32_t mx4_pack8(const float* x, int e) {
+  auto y = [&](float v) { return fminf(fmaxf(__builtin_amdgcn_ldexpf(v, -e), -6.0f), 6.0f); };
+  uint32_t pk = 0;
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y(x[0]), y(x[1]), 1.0f, 0);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y(x[2]), y(x[3]), 1.0f, 1);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y(x[4]), y(x[5]), 1.0f, 2);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y(x[6]), y(x[7]), 1.0f, 3);
+  return pk;
+}
+
 // Blocks of 32 channels: one thread per (token, block). Scales go to
 // [BH][srows][D / 32] with srows >= N rows per head (padding rows untouched).
-template <typename T, int D>
+// FP8: one code byte per element; FP4: two per byte, the even channel in
+// the low nibble (rows of D / 2 bytes).
+template <typename T, int D, bool FP4>
 __global__ void __launch_bounds__(256) quant_mx_rows_kernel(const T* __restrict__ x, int64_t BH,
                                                             int N, int srows,
                                                             uint8_t* __restrict__ codes,
@@ -63,23 +83,37 @@ __global__ void __launch_bounds__(256) quant_mx_rows_kernel(const T* __restrict_
   uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   uint8_t sb = 0;
   if (amax > 0.0f) {
-    const int e = mx_exp(amax);
+    const int e = FP4 ? mx4_exp(amax) : mx_exp(amax);
     sb = (uint8_t)(e + 127);
+    if constexpr (FP4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], e);
+      for (int i = 0; i < 4; ++i) w[i] = mx4_pack8(&v[8 * i], e);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], e);
+    }
   }
-  uint8_t* dst = codes + row * D + 32 * blk;
-  st16(dst, u32x4{w[0], w[1], w[2], w[3]});
-  st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+  if constexpr (FP4) {
+    st16(codes + row * (D / 2) + 16 * blk, u32x4{w[0], w[1], w[2], w[3]});
+  } else {
+    uint8_t* dst = codes + row * D + 32 * blk;
+    st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+    st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+  }
   scales[(bh * srows + tok) * NB + blk] = sb;
 }
 
 // Blocks of 32 tokens of one channel: one workgroup per (head, 64-token tile).
-// layout 0: codes [BH][N][D], scales [BH][ceil(N/32)][D] (blocks past N not
-//           written);
-// layout 1: codes as transposed tiles [BH][ceil(N/64)][D][64] with zero codes
-//           past N, scales [BH][2 ceil(N/64)][D] (a block past N: scale byte 0).
-template <typename T, int D>
+// FP8 (one code byte per element):
+//   layout 0: codes [BH][N][D], scales [BH][ceil(N/32)][D] (blocks past N not
+//             written);
+//   layout 1: codes as transposed tiles [BH][ceil(N/64)][D][64] with zero
+//             codes past N, scales [BH][2 ceil(N/64)][D] (a block past N:
+//             scale byte 0).
+// FP4 (two codes per byte, the lower index in the low nibble): layout 0
+// codes [BH][N][D / 2] (channel pairs), layout 1 transposed tiles
+// [BH][ceil(N/64)][D][32] (token pairs); scales as for FP8.
+template <typename T, int D, bool FP4>
 __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict__ x, int N,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
@@ -87,7 +121,7 @@ __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict_
   constexpr int CPR = D / 8;
   constexpr int TLD = D + 1;
   __shared__ float tile[64 * TLD];
-  __shared__ __attribute__((aligned(16))) uint8_t ctile[64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[64 * D];   // FP4: one nibble per byte
   const int nt = (N + 63) / 64;
   const int64_t bh = blockIdx.x / nt;
   const int t = (int)(blockIdx.x - bh * nt);
@@ -111,33 +145,72 @@ __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict_
     uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint8_t sb = 0;
     if (amax > 0.0f) {
-      const int e = mx_exp(amax);
+      const int e = FP4 ? mx4_exp(amax) : mx_exp(amax);
       sb = (uint8_t)(e + 127);
+      if constexpr (FP4) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float* col = &tile[(32 * j + 4 * q) * TLD + d];
-        w[q] = mx_pack4(col[0], col[TLD], col[2 * TLD], col[3 * TLD], e);   // rows past N are 0
+        for (int q = 0; q < 4; ++q) {
+          float col[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) col[b] = tile[(32 * j + 8 * q + b) * TLD + d];   // rows past N are 0
+          w[q] = mx4_pack8(col, e);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float* col = &tile[(32 * j + 4 * q) * TLD + d];
+          w[q] = mx_pack4(col[0], col[TLD], col[2 * TLD], col[3 * TLD], e);   // rows past N are 0
+        }
       }
     }
     if (layout == 1) {
-      uint8_t* dst = codes + ((bh * nt + t) * (int64_t)D + d) * 64 + 32 * j;
-      st16(dst, u32x4{w[0], w[1], w[2], w[3]});
-      st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+      if constexpr (FP4) {
+        st16(codes + ((bh * nt + t) * (int64_t)D + d) * 32 + 16 * j, u32x4{w[0], w[1], w[2], w[3]});
+      } else {
+        uint8_t* dst = codes + ((bh * nt + t) * (int64_t)D + d) * 64 + 32 * j;
+        st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+        st16(dst + 16, u32x4{w[4], w[5], w[6], w[7]});
+      }
       scales[((bh * nt + t) * 2 + j) * (int64_t)D + d] = sb;
     } else {
+      if constexpr (FP4) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) ctile[(32 * j + 4 * q + b) * D + d] = (uint8_t)(w[q] >> (8 * b));
+          for (int b = 0; b < 8; ++b) ctile[(32 * j + 8 * q + b) * D + d] = (uint8_t)((w[q] >> (4 * b)) & 15);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) ctile[(32 * j + 4 * q + b) * D + d] = (uint8_t)(w[q] >> (8 * b));
+      }
       if (cnt > 0) scales[(bh * nblk32 + 2 * t + j) * (int64_t)D + d] = sb;
     }
   }
   if (layout == 0) {
     __syncthreads();
-    for (int ch = threadIdx.x; ch < 64 * (D / 16); ch += 256) {
-      const int r = ch / (D / 16), c = ch - r * (D / 16);
-      if (r0 + r < N)
-        st16(codes + (bh * N + r0 + r) * (int64_t)D + 16 * c, *(const u32x4*)&ctile[r * D + 16 * c]);
+    if constexpr (FP4) {
+      // row r: D / 2 bytes, byte c = channels 2c (low nibble) and 2c + 1
+      for (int ch = threadIdx.x; ch < 64 * (D / 32); ch += 256) {
+        const int r = ch / (D / 32), c = ch - r * (D / 32);
+        if (r0 + r < N) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t wq = 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) wq |= (uint32_t)ctile[r * D + 32 * c + 8 * q + b] << (4 * b);
+            w4[q] = wq;
+          }
+          st16(codes + (bh * N + r0 + r) * (int64_t)(D / 2) + 16 * c, u32x4{w4[0], w4[1], w4[2], w4[3]});
+        }
+      }
+    } else {
+      for (int ch = threadIdx.x; ch < 64 * (D / 16); ch += 256) {
+        const int r = ch / (D / 16), c = ch - r * (D / 16);
+        if (r0 + r < N)
+          st16(codes + (bh * N + r0 + r) * (int64_t)D + 16 * c, *(const u32x4*)&ctile[r * D + 16 * c]);
+      }
     }
   }
 }
@@ -158,12 +231,38 @@ __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict_
 // Operand layout of the scaled FP8 MFMA (checked on the GPU): lane half h
 // holds k-slots 16 h + (0..15) in its bytes 0..15 and 32 + 16 h + (0..15) in
 // bytes 16..31; bytes 0..15 of both halves are scale block 0 (the scale comes
-// from lane half 0), bytes 16..31 block 1 (from lane half 1).
-template <typename TO, int D>
+// from lane half 0), bytes 16..31 block 1 (from lane half 1). With FP4
+// operands (E2M1, format 4) lane half h holds k-slots 32 h + (0..31) as the
+// nibbles of its first 16 bytes (nibble i: bits 4 (i % 8) of dword i / 8),
+// and its scale is that of block h. The FP4 x FP4 product runs at about
+// twice the FP8 rate; an FP4 x FP8 product runs at the FP8 rate.
+//
+// The diagonal-tiled mixed variant ("Diagonal-Tiled Mixed-Precision
+// Attention" of "Transformers Get a Turbo Boost with Mixed-Precision Magic",
+// section "The DMA breakthrough": two low-bit MXFP products chosen per tile,
+// the diagonal apart) runs in two passes of this kernel. A wave's 32 rows
+// form one row block; the key tiles holding the positions of its rows (1 or
+// 2) are its diagonal tiles.
+//   PASS 1: every tile but the wave's diagonal ones (masked out), in MXFP4:
+//           V from its MXFP4 copy (blocks of 32 keys of one channel), the
+//           weights of each 32-key block with scale 2^E, E = floor(log2
+//           block max) - 2, clamped to 6 and rounded to E2M1. The K rows are
+//           permuted so that lane half h holds the scores of keys 32 h +
+//           (0..31), the k-slots of the FP4 operand. Writes O / l, m and l
+//           of every row in fp32 to the partial buffer.
+//   PASS 2: only the workgroup's diagonal tiles, each wave keeping its own,
+//           in MXFP8 as in the MX mode; merges its result with the row's
+//           pass 1 partial by log-sum-exp weights and writes O.
+// Both passes keep the running maximum an integer, so a block's scale and
+// its rounded weights do not depend on when the maximum was last raised, and
+// splitting the keys over two passes changes no rounding.
+template <typename TO, int D, int PASS>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float* __restrict__ qs,
                   const int8_t* __restrict__ kc, const float* __restrict__ ks,
-                  const uint8_t* __restrict__ vct, const uint8_t* __restrict__ vs) {
+                  const uint8_t* __restrict__ vct, const uint8_t* __restrict__ vs,
+                  float* __restrict__ part) {
+  constexpr bool FP4 = PASS == 1;   // V^T tiles of D rows x 32 bytes (E2M1 pairs)
   constexpr int BM = 128;
   constexpr int KS = D / 32;       // i8 k-steps (32 channels each)
   constexpr int DB = D / 32;       // 32-channel blocks of O^T
@@ -172,7 +271,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
   constexpr float kLag = 2.0f;     // the running maximum may trail by this (log2)
   constexpr float kOff = 12582912.0f;   // 1.5 * 2^23
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t sv[2][FP4 ? D * 32 : D * 64];
   __shared__ __attribute__((aligned(16))) uint8_t svs[2][2 * D];   // V scales [block][channel]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -189,15 +288,25 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
   const int8_t* Qc = qc + (int64_t)bh * a.Nq * D;
   const int8_t* Kc = kc + (int64_t)bg * a.Nk * D;
   const float* Ks = ks + (int64_t)bg * nkt;
-  const uint8_t* Vt = vct + (int64_t)bg * nkt * D * 64;
+  const uint8_t* Vt = vct + (int64_t)bg * nkt * D * (FP4 ? 32 : 64);
   const uint8_t* Vs = vs + (int64_t)bg * nkt * 2 * D;
   TO* Op = (TO*)a.o + (int64_t)bh * a.Nq * D;
 
   const int qlast = min(q0 + BM, a.Nq) - 1;
   const int kv_lo = a.window_w > 0 ? max(a.window_lo, a.pos0 + q0 - a.window_w + 1) : a.window_lo;
   const int kv_hi = a.causal ? min(a.Nk, a.pos0 + qlast + 1) : a.Nk;
-  const int t_lo = kv_lo / 64;
-  const int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
+  int t_lo = kv_lo / 64;
+  int nt = kv_hi > kv_lo ? (kv_hi + 63) / 64 - t_lo : 0;
+  // the diagonal key tiles of the workgroup's 128 rows and of this wave's 32
+  const int64_t gpos = (int64_t)a.pos0 + q0, wpos = (int64_t)a.pos0 + q0 + 32 * wave;
+  const int64_t wd_lo = wpos / 64, wd_hi = (wpos + 31) / 64;
+  if constexpr (PASS == 2) {
+    // only the workgroup's diagonal tiles that hold visible keys
+    const int g_lo = (int)min(max(gpos / 64, (int64_t)t_lo), (int64_t)(t_lo + nt));
+    const int g_hi = (int)min(max((gpos + 127) / 64 + 1, (int64_t)g_lo), (int64_t)(t_lo + nt));
+    t_lo = g_lo;
+    nt = g_hi - g_lo;
+  }
 
   const int qrow = q0 + wave * 32 + col;
   const int qw0 = q0 + wave * 32;
@@ -227,8 +336,11 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
   // V^T row d at c ^ vswz(d).
   auto kswz = [](int r) { return KCPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
   auto vswz = [](int d) { return (d >> 2) & 3; };
-  auto kperm = [](int r) { return 32 * (r >> 5) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3); };
-  constexpr int NK = 16 / KRPI, NV = D / 64;
+  auto kperm = [](int r) {
+    return FP4 ? 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3)
+               : 32 * (r >> 5) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
+  };
+  constexpr int NK = 16 / KRPI, NV = FP4 ? 1 : D / 64;
   uint32_t kofs[NK], vofs[NV];
 #pragma unroll
   for (int u = 0; u < NK; ++u) {
@@ -238,7 +350,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     const int d = (D / 4) * wave + 16 * u + lane / 4, pos = lane % 4;
-    vofs[u] = (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
+    vofs[u] = FP4 ? (uint32_t)(16 * lane) : (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
   }
   constexpr int NVS = 2 * D / 16;   // 16-byte pieces of a V scale tile
   auto load_k = [&](int t, int buf) {
@@ -257,9 +369,15 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     }
   };
   auto load_v = [&](int t, int buf) {
-    const uint8_t* base = Vt + (int64_t)t * D * 64;
+    if constexpr (FP4) {
+      // D x 32 contiguous bytes: 1 KB per wave (waves 0-1 at head dim 64)
+      if (D == 128 || wave < 2)
+        load_to_lds16(Vt + (int64_t)t * D * 32 + 1024 * wave, vofs[0], &sv[buf][1024 * wave]);
+    } else {
+      const uint8_t* base = Vt + (int64_t)t * D * 64;
 #pragma unroll
-    for (int u = 0; u < NV; ++u) load_to_lds16(base, vofs[u], &sv[buf][((D / 4) * wave + 16 * u) * 64]);
+      for (int u = 0; u < NV; ++u) load_to_lds16(base, vofs[u], &sv[buf][((D / 4) * wave + 16 * u) * 64]);
+    }
     // the tile's 2 D scale bytes ride along (wave 1)
     // (the byte offset is rebuilt from the lane id on the spot: kept across
     // the loop, it is spilled at head dim 128)
@@ -295,10 +413,10 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       }
   };
 
-  // E4M3 1.0 in every byte, and a zero accumulator
+  // E4M3 (pass 1: E2M1) 1.0 in every byte (nibble), and a zero accumulator
   i32x8 ones8;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ones8[j] = 0x38383838;
+  for (int j = 0; j < 8; ++j) ones8[j] = FP4 ? 0x22222222 : 0x38383838;
   f32x16 fzero;
 #pragma unroll
   for (int j = 0; j < 16; ++j) fzero[j] = 0.0f;
@@ -315,27 +433,51 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
       for (int j = 0; j < 16; ++j) sf[mb][j] = __builtin_bit_cast(f32x16, cur[mb])[j];
     const int k0 = 64 * t;
+    if constexpr (PASS != 0) {
+      // pass 1 leaves out the wave's diagonal tiles, pass 2 keeps only them
+      const bool dg = t >= wd_lo && t <= wd_hi;
+      if (PASS == 1 ? dg : !dg) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sf[mb][j] = -INFINITY;
+      }
+    }
     if (k0 < wave_lo || k0 + 63 > wave_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = k0 + 32 * mb + 16 * half + 4 * (j >> 2) + (j & 3);
+          const int key = FP4 ? k0 + 32 * half + 16 * mb + 4 * (j >> 2) + (j & 3)
+                              : k0 + 32 * mb + 16 * half + 4 * (j >> 2) + (j & 3);
           if (key < row_lo || key > row_hi) sf[mb][j] = -INFINITY;
         }
     }
-    float bm[2];   // per 32-key block: the lane's largest kOff + S
+    // per 32-key block: the largest kOff + S (pass 1: the lane holds all 32
+    // keys of its block h, bm[0] = bm[1])
+    float bm[2], rowm;
+    if constexpr (FP4) {
+      float b = sf[0][0];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      bm[mb] = sf[mb][0];
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 1; j < 16; ++j) bm[mb] = fmaxf(bm[mb], sf[mb][j]);
-      bm[mb] = halves_max(bm[mb]);
+        for (int j = 0; j < 16; ++j) b = fmaxf(b, sf[mb][j]);
+      bm[0] = bm[1] = b;
+      rowm = halves_max(b);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        bm[mb] = sf[mb][0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) bm[mb] = fmaxf(bm[mb], sf[mb][j]);
+        bm[mb] = halves_max(bm[mb]);
+      }
+      rowm = fmaxf(bm[0], bm[1]);
     }
-    const float mx = (fmaxf(bm[0], bm[1]) - kOff) * cf;   // exact subtraction
+    const float mx = (rowm - kOff) * cf;   // exact subtraction
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLag)) {
       asm volatile("" ::: "memory");
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = PASS != 0 ? ceilf(fmaxf(m_run, mx)) : fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -348,9 +490,11 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     // exponent = S cf - mu = (kOff + S) cf - (kOff cf + mu): one FMA per
     // score; the rounding of kOff cf + mu (< 0.9 cf + 2^-21) is far below the
     // INT8 rounding of the scores for cf < 0.03, larger factors take the
-    // exact form.
+    // exact form. The diagonal-tiled passes always take it: a common error of
+    // that size would move weights across E2M1 rounding midpoints (steps of
+    // up to a third of a weight) that the exact exponent keeps.
     float C = fmaf(kOff, cf, mu);
-    if (cf >= 0.03f) {
+    if (PASS != 0 || cf >= 0.03f) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -369,7 +513,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const float x = fmaf(bm[mb], cf, -C);
-      E[mb] = bm[mb] == -INFINITY ? -127 : max((int)__builtin_floorf(x) - 7, -127);
+      E[mb] = bm[mb] == -INFINITY ? -127 : max((int)__builtin_floorf(x) - (FP4 ? 2 : 7), -127);
       Cm[mb] = C + (float)E[mb];   // exact: C's ulp is below 1 and E an integer
     }
 
@@ -377,21 +521,42 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     // work, then the MFMAs; the other wave of the SIMD fills the gaps).
     s_mma((i + 1) & 1, nxt);
     i32x8 pb;
+    if constexpr (FP4) {
+      // E2M1 weights clamped to 6, nibble 16 mb + j = key 32 h + 16 mb + j
+      // (FP4 operands read dwords 0..3 only)
+      asm volatile("" : "=v"(pb));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float e[4];
+        for (int w = 0; w < 2; ++w) {
+          float e[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -Cm[mb]));
-        // (the second conversion writes the upper half, so the first one may
-        // start from whatever the register holds: no zeroing move)
-        int pk;
-        asm volatile("" : "=v"(pk));
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
-        pb[4 * mb + q4] = pk;
-      }
+          for (int k = 0; k < 8; ++k)
+            e[k] = fminf(__builtin_amdgcn_exp2f(fmaf(sf[mb][8 * w + k], cf, -Cm[0])), 6.0f);
+          uint32_t pk = 0;
+          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[0], e[1], 1.0f, 0);
+          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[2], e[3], 1.0f, 1);
+          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[4], e[5], 1.0f, 2);
+          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, e[6], e[7], 1.0f, 3);
+          pb[2 * mb + w] = (int)pk;
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float e[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(sf[mb][4 * q4 + k], cf, -Cm[mb]));
+          // (the second conversion writes the upper half, so the first one may
+          // start from whatever the register holds: no zeroing move)
+          int pk;
+          asm volatile("" : "=v"(pk));
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk, true);
+          pb[4 * mb + q4] = pk;
+        }
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 80, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
@@ -399,7 +564,8 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     // The denominator: the tile's row sums of the weights the numerator uses,
     // in unscaled units, from one more scaled MFMA against an all-ones block
     // (every row of the product is the same column sum).
-    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pb, fzero, 0, 0, 0, 127, 0, psc);
+    constexpr int fmt = FP4 ? 4 : 0;   // E2M1 or E4M3 operands
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pb, fzero, fmt, fmt, 0, 127, 0, psc);
 
     // O^T += V^T P^T for tile i: one scaled FP8 MFMA per 32 channels (a
     // scheduling fence keeps the V operand reads from being hoisted above
@@ -409,13 +575,23 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = 32 * db + col;
-      const uint8_t* row = &sv[vb][d * 64];
-      const u32x4 lo = ld16(row + 16 * (half ^ vswz(d)));         // keys 16 h + (0..15)
-      const u32x4 hi = ld16(row + 16 * ((2 + half) ^ vswz(d)));   // keys 32 + 16 h + (0..15)
-      const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      i32x8 va;
+      if constexpr (FP4) {
+        const u32x4 x = ld16(&sv[vb][d * 32 + 16 * half]);   // keys 32 h + (0..31)
+        asm volatile("" : "=v"(va));
+        va[0] = (int)x[0];
+        va[1] = (int)x[1];
+        va[2] = (int)x[2];
+        va[3] = (int)x[3];
+      } else {
+        const uint8_t* row = &sv[vb][d * 64];
+        const u32x4 lo = ld16(row + 16 * (half ^ vswz(d)));         // keys 16 h + (0..15)
+        const u32x4 hi = ld16(row + 16 * ((2 + half) ^ vswz(d)));   // keys 32 + 16 h + (0..15)
+        va = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
       const int vsc = svs[vb][half * D + d];
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, vsc, 0, psc);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], fmt, fmt, 0, vsc, 0, psc);
     }
     l_run += rs[0];
     vmem_wait_all();
@@ -441,53 +617,93 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 
   const float l = l_run;   // both lane halves hold the row's full sum
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  if (qrow < a.Nq) {
-    TO* orow = Op + (int64_t)qrow * D;
+  if (qrow >= a.Nq) return;
+  // the partial of row qrow (diagonal-tiled passes): O / l in channels 0..D-1,
+  // then m (exp2 units, an integer or -inf) and l
+  float* prow = part + ((int64_t)bh * a.Nq + qrow) * (D + 4);
+  if constexpr (PASS == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d = 32 * db + 8 * a4 + 4 * half;
-        TO o4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][4 * a4 + r] * inv);
-        *(u32x2*)(orow + d) = *(const u32x2*)o4;
+        *(f32x4*)(prow + d) = f32x4{oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
+                                    oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
       }
+    if (half == 0) *(f32x4*)(prow + D) = f32x4{m_run, l, 0.0f, 0.0f};
+    return;
   }
+  float w1 = 0.0f, w2 = 1.0f;   // the weights of the pass 1 partial and of this result
+  if constexpr (PASS == 2) {
+    const f32x4 ml = *(const f32x4*)(prow + D);
+    const float M = fmaxf(ml[0], m_run);
+    w1 = ml[0] == -INFINITY ? 0.0f : ml[1] * __builtin_amdgcn_exp2f(ml[0] - M);
+    w2 = m_run == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m_run - M);
+    const float L = w1 + w2;
+    const float r = L > 0.0f ? 1.0f / L : 0.0f;
+    w1 *= r;
+    w2 *= r;
+  }
+  TO* orow = Op + (int64_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * db + 8 * a4 + 4 * half;
+      float o1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (PASS == 2) {
+        const f32x4 p = *(const f32x4*)(prow + d);
+        o1[0] = p[0]; o1[1] = p[1]; o1[2] = p[2]; o1[3] = p[3];
+      }
+      TO o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(fmaf(w2, oacc[db][4 * a4 + r] * inv, w1 * o1[r]));
+      *(u32x2*)(orow + d) = *(const u32x2*)o4;
+    }
 }
 
 template <typename TO, int D>
 hipError_t prefill_mx_t(const FwdArgs& a, const int8_t* qc, const float* qs, const int8_t* kc,
-                        const float* ks, const uint8_t* vct, const uint8_t* vs, hipStream_t st) {
+                        const float* ks, const uint8_t* vct, const uint8_t* vs, const uint8_t* v4t,
+                        const uint8_t* v4s, float* part, hipStream_t st) {
   const int ntq = (a.Nq + 127) / 128;
   const int64_t grid = (int64_t)a.B * a.Hq * ntq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_mx_kernel<TO, D>), dim3((unsigned)grid), dim3(256), 0, st, a, ntq,
-                     qc, qs, kc, ks, vct, vs);
+  if (v4t == nullptr) {
+    hipLaunchKernelGGL((prefill_mx_kernel<TO, D, 0>), dim3((unsigned)grid), dim3(256), 0, st, a, ntq,
+                       qc, qs, kc, ks, vct, vs, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_mx_kernel<TO, D, 1>), dim3((unsigned)grid), dim3(256), 0, st, a, ntq,
+                     qc, qs, kc, ks, v4t, v4s, part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_mx_kernel<TO, D, 2>), dim3((unsigned)grid), dim3(256), 0, st, a, ntq,
+                     qc, qs, kc, ks, vct, vs, part);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool FP4>
 hipError_t quant_mx_t(const void* x, int64_t BH, int N, int D, int axis, int layout, int srows,
                       uint8_t* codes, uint8_t* scales, hipStream_t st) {
   if (axis == 0) {
     const int64_t blocks = (BH * N * (D / 32) + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (D == 64)
-      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 64>), dim3((unsigned)blocks), dim3(256), 0, st,
-                         (const T*)x, BH, N, srows, codes, scales);
+      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 64, FP4>), dim3((unsigned)blocks), dim3(256), 0,
+                         st, (const T*)x, BH, N, srows, codes, scales);
     else
-      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 128>), dim3((unsigned)blocks), dim3(256), 0, st,
-                         (const T*)x, BH, N, srows, codes, scales);
+      hipLaunchKernelGGL((quant_mx_rows_kernel<T, 128, FP4>), dim3((unsigned)blocks), dim3(256), 0,
+                         st, (const T*)x, BH, N, srows, codes, scales);
   } else {
     const int64_t grid = BH * ((N + 63) / 64);
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (D == 64)
-      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st,
+      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 64, FP4>), dim3((unsigned)grid), dim3(256), 0, st,
                          (const T*)x, N, codes, scales, layout);
     else
-      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st,
-                         (const T*)x, N, codes, scales, layout);
+      hipLaunchKernelGGL((quant_mx_cols_kernel<T, 128, FP4>), dim3((unsigned)grid), dim3(256), 0,
+                         st, (const T*)x, N, codes, scales, layout);
   }
   return hipGetLastError();
 }
@@ -495,19 +711,23 @@ hipError_t quant_mx_t(const void* x, int64_t BH, int N, int D, int axis, int lay
 }  // namespace
 
 hipError_t launch_quant_mx(const void* x, int elem, int64_t BH, int N, int D, int axis, int layout,
-                           int srows, uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  return elem == 2 ? quant_mx_t<__bf16>(x, BH, N, D, axis, layout, srows, codes, scales, s)
-                   : quant_mx_t<_Float16>(x, BH, N, D, axis, layout, srows, codes, scales, s);
+                           int srows, uint8_t* codes, uint8_t* scales, hipStream_t s, bool fp4) {
+  if (fp4)
+    return elem == 2 ? quant_mx_t<__bf16, true>(x, BH, N, D, axis, layout, srows, codes, scales, s)
+                     : quant_mx_t<_Float16, true>(x, BH, N, D, axis, layout, srows, codes, scales, s);
+  return elem == 2 ? quant_mx_t<__bf16, false>(x, BH, N, D, axis, layout, srows, codes, scales, s)
+                   : quant_mx_t<_Float16, false>(x, BH, N, D, axis, layout, srows, codes, scales, s);
 }
 
 hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs,
                              const int8_t* kc, const float* ks, const uint8_t* vct,
-                             const uint8_t* vs, int elem_out, hipStream_t s) {
+                             const uint8_t* vs, const uint8_t* v4t, const uint8_t* v4s,
+                             float* part, int elem_out, hipStream_t s) {
   if (elem_out == 2)
-    return a.D == 64 ? prefill_mx_t<__bf16, 64>(a, qc, qs, kc, ks, vct, vs, s)
-                     : prefill_mx_t<__bf16, 128>(a, qc, qs, kc, ks, vct, vs, s);
-  return a.D == 64 ? prefill_mx_t<_Float16, 64>(a, qc, qs, kc, ks, vct, vs, s)
-                   : prefill_mx_t<_Float16, 128>(a, qc, qs, kc, ks, vct, vs, s);
+    return a.D == 64 ? prefill_mx_t<__bf16, 64>(a, qc, qs, kc, ks, vct, vs, v4t, v4s, part, s)
+                     : prefill_mx_t<__bf16, 128>(a, qc, qs, kc, ks, vct, vs, v4t, v4s, part, s);
+  return a.D == 64 ? prefill_mx_t<_Float16, 64>(a, qc, qs, kc, ks, vct, vs, v4t, v4s, part, s)
+                   : prefill_mx_t<_Float16, 128>(a, qc, qs, kc, ks, vct, vs, v4t, v4s, part, s);
 }
 
 }  // namespace attn

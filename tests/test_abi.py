@@ -50,6 +50,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_workspace_bytes", "attn_quantize_qk",
               "attn_quantize_v", "attn_decode_kvq", "attn_decode_kvq_workspace_bytes",
               "attn_fwd_sliding", "attn_fwd_sliding_workspace_bytes", "attn_quantize_mx",
+              "attn_quantize_mx4",
               "attn_fwd_rope", "attn_fwd_rope_workspace_bytes", "attn_fwd_decode",
               "attn_fwd_decode_workspace_bytes", "attn_fwd_plan", "attn_fwd_noalloc",
               "attn_status_string"):
@@ -105,6 +106,9 @@ def _fwd(lib, **kw):
     (dict(D=256), E_UNSUPPORTED),
     (dict(dtype=7), E_UNSUPPORTED),
     (dict(mode=5), E_UNSUPPORTED),
+    (dict(mode=4), E_UNSUPPORTED),
+    (dict(mode=3, dtype=0), E_UNSUPPORTED),   # the diagonal-tiled MX mode needs 16-bit inputs
+    (dict(mode=3), E_WORKSPACE),
     (dict(mode=1, dtype=0), E_UNSUPPORTED),   # quantised mode needs 16-bit inputs
     (dict(dtype=0), E_WORKSPACE),             # fp32 inputs need a bf16 staging workspace
     (dict(mode=1), E_WORKSPACE),
@@ -280,6 +284,17 @@ def test_mx_entry_points_reject_before_enqueue(lib):
     # INT8 codes of Q and K, E4M3 codes of V (1 byte each), V's scale bytes (one
     # per 32 keys of a channel) and the fp32 scales of Q's and K's 64-token blocks
     assert need >= 3 * 40 * 32760 * 128 + 40 * 32760 * 128 // 32 + 2 * 40 * 512 * 4
+    # the FP4 quantiser: the same checks
+    q4 = lib.attn_quantize_mx4
+    assert q4(None, FAKE, FAKE, 1, 2, 64, 128, 0, 2, None) == E_INVALID
+    assert q4(FAKE, FAKE, FAKE, 1, 2, 64, 96, 0, 2, None) == E_UNSUPPORTED
+    assert q4(FAKE, FAKE, FAKE, 1, 2, 64, 128, 0, 0, None) == E_UNSUPPORTED
+    assert q4(FAKE, FAKE, FAKE, 1, 2, 64, 128, 2, 2, None) == E_INVALID
+    assert q4(FAKE, FAKE + 4, FAKE, 1, 2, 64, 128, 1, 2, None) == E_INVALID   # misaligned codes
+    # the diagonal-tiled mode also holds V's MXFP4 codes (half a byte per element)
+    # and scale bytes, and the fp32 row partials (D + 4 floats per query row)
+    need3 = ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 3, 2)
+    assert need3 >= need + 40 * 32760 * 128 // 2 + 40 * 32760 * 128 // 32 + 40 * 32760 * 132 * 4
 
 
 
@@ -451,6 +466,12 @@ def test_dispatch_boundaries(lib):
     p = _plan(B=65535, Hq=2, Hkv=1, Nq=1, Nk=4096, D=128, dtype=1)
     assert p.kernel == sdpa.KERNEL_DECODE
     assert sdpa.fwd_workspace_bytes(70000, 2, 1, 1, 4096, 128, dtype=f16) == 0
+    # the opt-in low-precision modes: one 128-row workgroup per query tile
+    p = _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=128, mode=sdpa.MODE_MXD)
+    assert (p.kernel, p.waves, p.rows, p.workgroups, p.pre_launches) == \
+        (sdpa.KERNEL_PREFILL_MXD, 4, 128, 4, 4)
+    assert _plan(B=1, Hq=2, Hkv=2, Nq=256, Nk=256, D=128, mode=sdpa.MODE_MX).kernel == \
+        sdpa.KERNEL_PREFILL_MX
     # eight-wave prefill only for head dim 128 and grids of at least one round of
     # 256 workgroups whose last round is full, more than half full, or amortised
     # over eight rounds
