@@ -1,6 +1,7 @@
 """A seeded sweep of small random shapes through attn_fwd / attn_fwd_sliding
-(and attn_fwd_rope with random rotary settings, and attn_decode_kvq over random
-quantised caches), every output row against the fp64 oracle.
+(and attn_fwd_rope with random rotary settings, attn_decode_kvq over random
+quantised caches, and the diagonal-tiled MX mode against the oracle's
+emulation of it), every output row against the fp64 oracle.
 
 The hand-picked cases elsewhere pin the corners one by one; this sweep draws
 the arguments together (batch, GQA group, ragged query and key counts, head
@@ -17,7 +18,9 @@ import torch
 import scaled_dot_product_amd as sdpa
 from scaled_dot_product_amd.inputs import Workload
 
-from _parity import check_kvq, check_rope, check_workload, masked_rows
+import oracle
+
+from _parity import announce, check_kvq, check_rope, check_workload, gpu_fwd, masked_rows, metrics
 
 pytestmark = pytest.mark.gpu
 
@@ -157,3 +160,47 @@ KVQ_CASES = _kvq_cases()
 @pytest.mark.parametrize("w", KVQ_CASES, ids=[_id(w) for w in KVQ_CASES])
 def test_sweep_kvq_case_matches_oracle(w):
     check_kvq(w)
+
+
+N_MXD = 25
+
+
+def _mxd_cases():
+    rng = np.random.RandomState(SEED + 3)
+    out = []
+    for n in range(N_MXD):
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        Nq = int(rng.randint(1, 300))
+        Nk = int(rng.randint(1, 800))
+        causal = bool(rng.rand() < 0.5)
+        pos0 = int(rng.choice([0, max(0, Nk - Nq), rng.randint(0, Nk)]))
+        kind = rng.choice(["none", "lo", "w"])
+        window_lo = int(rng.randint(0, Nk)) if kind == "lo" else 0
+        window_w = int(rng.randint(1, Nk + 1)) if kind == "w" else 0
+        dt = [torch.bfloat16, torch.float16][int(rng.randint(2))]
+        out.append(Workload(f"mxd_sweep{n}", int(rng.choice([1, 2])), Hkv * G, Hkv, Nq, Nk, D, dt,
+                            causal=causal, window_lo=window_lo, pos0=pos0, mode=3,
+                            window_w=window_w))
+    return out
+
+
+MXD_CASES = _mxd_cases()
+
+
+@pytest.mark.parametrize("w", MXD_CASES, ids=[_id(w) for w in MXD_CASES])
+def test_sweep_mxd_case_matches_emulation(w):
+    # the mode's own reference rounds every weight as the mode does: held to
+    # 1e-2 relative (output rounding 2^-9); rows with no visible key are zeros
+    from scaled_dot_product_amd.inputs import make_qkv
+    announce(f"{_id(w)}")
+    q, k, v = make_qkv(w)
+    out = gpu_fwd(w, q, k, v).double().cpu()
+    ref = oracle.attn_mxd(q, k, v, scale=w.scale, causal=w.causal, window_lo=w.window_lo,
+                          pos0=w.pos0, window_w=w.window_w)
+    rel, _ = metrics(out.numpy(), ref)
+    print(f"    rel={rel:.3e}", flush=True)
+    assert rel <= 1e-2, rel
+    for i in masked_rows(w):
+        assert torch.all(out[:, :, i] == 0), i
