@@ -171,3 +171,30 @@ def test_mxd_mode_video_dit_sampled():
         print(f"    head {h}: rel(vs emulation)={rel:.3e} rel(vs exact)={rel_ex:.3e}", flush=True)
         assert rel <= MXD_REL, rel
         assert rel_ex <= MXD_EXACT, rel_ex
+
+
+def test_mxd_mode_with_rope():
+    # attn_fwd_rope in the diagonal-tiled mode: Q and K are turned inside the
+    # INT8 quantiser. Against exact attention on the rotated inputs (the mode's
+    # own error), and against the mode's emulation on the oracle's rotation
+    # rounded to fp32: the two rotations differ in their last bits, which may
+    # move an INT8 code by one step, so this comparison gets twice the bar
+    w = Workload("mxd_rope", 1, 2, 2, 300, 300, 128, BF, causal=True, mode=sdpa.MODE_MXD)
+    q, k, v = make_qkv(w)
+    plain = dict(style=0, scaling=0, base=10000.0)
+    announce(f"mxd rope {plain}")
+    dev = torch.device("cuda:0")
+    out = sdpa.fwd_rope(q.to(dev), k.to(dev), v.to(dev), sdpa.Rope(**plain), causal=True,
+                        scale=w.scale, mode=sdpa.MODE_MXD)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    ex = oracle.attn_rope(q, k, v, scale=w.scale, causal=True, **plain)
+    theta, _ = oracle.rope_freqs(w.D, base=10000.0)
+    qr = torch.from_numpy(oracle.rope_apply(q, 0, theta)).float()
+    kr = torch.from_numpy(oracle.rope_apply(k, 0, theta)).float()
+    ref = oracle.attn_mxd(qr, kr, v.float(), scale=w.scale, causal=True)
+    rel, _ = metrics(got, ref)
+    rel_ex, _ = metrics(got, ex)
+    print(f"    rel(vs emulation on rotated inputs)={rel:.3e} rel(vs exact)={rel_ex:.3e}", flush=True)
+    assert rel <= 2 * MXD_REL, rel
+    assert rel_ex <= MXD_EXACT, rel_ex
