@@ -350,7 +350,12 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     const int d = (D / 4) * wave + 16 * u + lane / 4, pos = lane % 4;
-    vofs[u] = FP4 ? (uint32_t)(16 * lane) : (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
+    // FP4: the tile's 16-byte chunk (row d, half h) sits at global chunk 2 d + h
+    // and at LDS chunk 32 (d / 16) + 16 h + d % 16, so that the 16 lanes of
+    // one LDS access read 256 contiguous bytes (conflict-free); lane i of the
+    // wave lands LDS chunk 64 wave + i and reads the matching global chunk
+    vofs[u] = FP4 ? (uint32_t)(16 * (32 * (lane >> 5) + 2 * (lane & 15) + ((lane >> 4) & 1)))
+                  : (uint32_t)(d * 64 + 16 * (pos ^ vswz(d)));
   }
   constexpr int NVS = 2 * D / 16;   // 16-byte pieces of a V scale tile
   auto load_k = [&](int t, int buf) {
@@ -577,7 +582,8 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
       const int d = 32 * db + col;
       i32x8 va;
       if constexpr (FP4) {
-        const u32x4 x = ld16(&sv[vb][d * 32 + 16 * half]);   // keys 32 h + (0..31)
+        // keys 32 h + (0..31) of channel d: LDS chunk 32 (d / 16) + 16 h + d % 16
+        const u32x4 x = ld16(&sv[vb][16 * (32 * (d >> 4) + 16 * half + (d & 15))]);
         asm volatile("" : "=v"(va));
         va[0] = (int)x[0];
         va[1] = (int)x[1];
