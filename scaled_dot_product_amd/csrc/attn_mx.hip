@@ -1,5 +1,5 @@
-// attn_mx.hip — the MX variant: OCP Microscaling FP8 blocks on the scaled
-// FP8 matrix cores of gfx950.
+// attn_mx.hip — the MX variants: OCP Microscaling FP8 (and FP4) blocks on
+// the scaled matrix cores of gfx950.
 //
 // The table in section 1 of "Attention kernels on a home RTX 5080" puts
 // per-block-scaled low-precision kernels at the top of its speed list, and
@@ -16,7 +16,9 @@
 // the 6 % budget.
 //
 // MX quantisation follows the OCP rule: e = floor(log2 amax) - 8, code =
-// E4M3(clamp(x * 2^-e, +-448)) rounded to nearest even.
+// E4M3(clamp(x * 2^-e, +-448)) rounded to nearest even; with FP4 (E2M1)
+// elements, for the diagonal-tiled variant below, e = floor(log2 amax) - 2
+// and code = E2M1(clamp(x * 2^-e, +-6)), two codes per byte.
 #include "attn_common.hpp"
 #include "attn_internal.hpp"
 
