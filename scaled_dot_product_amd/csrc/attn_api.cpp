@@ -113,7 +113,7 @@ Layout plan_layout(const FwdArgs& a, int mode, int dtype, int force_decode = -1,
     if (mode == ATTN_MODE_MXD) {
       L.v4c = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 32 * a.D);
       L.v4s = off; off = round_up(off + (size_t)a.B * a.Hkv * tiles * 2 * a.D);
-      L.part = off; off = round_up(off + (size_t)a.B * a.Hq * a.Nq * (a.D + 4) * 4);
+      L.part = off; off = round_up(off + (size_t)a.B * a.Hq * a.Nq * (a.D * 2 + 16));
     }
     L.total = off;
     return L;

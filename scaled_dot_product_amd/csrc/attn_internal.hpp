@@ -133,7 +133,8 @@ hipError_t launch_quant_mx(const void* x, int elem, int64_t BH, int N, int D, in
 // Q and K as per-64-token INT8 blocks (launch_quant_int8), V as MXFP8
 // transposed tiles + scale bytes (axis 1, layout 1); with v4t (MXFP4 tiles)
 // and v4s non-null, the diagonal-tiled mixed variant in two launches, which
-// pass per-row partials through `part` (fp32 [B][Hq][Nq][D + 4]).
+// pass per-row partials through `part` ([B][Hq][Nq] rows of D output-type
+// elements and 4 floats).
 hipError_t launch_prefill_mx(const FwdArgs& a, const int8_t* qc, const float* qs,
                              const int8_t* kc, const float* ks, const uint8_t* vct,
                              const uint8_t* vs, const uint8_t* v4t, const uint8_t* v4s,

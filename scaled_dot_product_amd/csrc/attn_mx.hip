@@ -217,6 +217,15 @@ __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict_
   }
 }
 
+// Four consecutive elements of a row in the output type, as floats.
+template <typename TO>
+__device__ __forceinline__ void get4(const TO* p, float (&v)[4]) {
+  const u32x2 x = *(const u32x2*)p;
+  const TO* e = (const TO*)&x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = (float)e[r];
+}
+
 // ---------------------------------------------------------------------------
 // MX attention: the quantised kernel's skeleton (4 waves x 32 query rows,
 // 64-key tiles, two workgroups per CU, code tiles by direct loads into
@@ -250,8 +259,8 @@ __global__ void __launch_bounds__(256) quant_mx_cols_kernel(const T* __restrict_
 //           weights of each 32-key block with scale 2^E, E = floor(log2
 //           block max) - 2, clamped to 6 and rounded to E2M1. The K rows are
 //           permuted so that lane half h holds the scores of keys 32 h +
-//           (0..31), the k-slots of the FP4 operand. Writes O / l, m and l
-//           of every row in fp32 to the partial buffer.
+//           (0..31), the k-slots of the FP4 operand. Writes O / l (in the
+//           output type), m and l (fp32) of every row to the partial buffer.
 //   PASS 2: only the workgroup's diagonal tiles, each wave keeping its own,
 //           in MXFP8 as in the MX mode; merges its result with the row's
 //           pass 1 partial by log-sum-exp weights and writes O.
@@ -627,24 +636,28 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
   const float l = l_run;   // both lane halves hold the row's full sum
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (qrow >= a.Nq) return;
-  // the partial of row qrow (diagonal-tiled passes): O / l in channels 0..D-1,
-  // then m (exp2 units, an integer or -inf) and l
-  float* prow = part + ((int64_t)bh * a.Nq + qrow) * (D + 4);
+  // the partial of row qrow (diagonal-tiled passes), D * sizeof(TO) + 16
+  // bytes: O / l in the output type, then m (exp2 units, an integer or -inf)
+  // and l in fp32
+  TO* prow = (TO*)((char*)part + ((int64_t)bh * a.Nq + qrow) * (D * (int)sizeof(TO) + 16));
+  float* pml = (float*)(prow + D);
   if constexpr (PASS == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d = 32 * db + 8 * a4 + 4 * half;
-        *(f32x4*)(prow + d) = f32x4{oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
-                                    oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
+        TO o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(oacc[db][4 * a4 + r] * inv);
+        *(u32x2*)(prow + d) = *(const u32x2*)o4;
       }
-    if (half == 0) *(f32x4*)(prow + D) = f32x4{m_run, l, 0.0f, 0.0f};
+    if (half == 0) *(f32x4*)pml = f32x4{m_run, l, 0.0f, 0.0f};
     return;
   }
   float w1 = 0.0f, w2 = 1.0f;   // the weights of the pass 1 partial and of this result
   if constexpr (PASS == 2) {
-    const f32x4 ml = *(const f32x4*)(prow + D);
+    const f32x4 ml = *(const f32x4*)pml;
     const float M = fmaxf(ml[0], m_run);
     w1 = ml[0] == -INFINITY ? 0.0f : ml[1] * __builtin_amdgcn_exp2f(ml[0] - M);
     w2 = m_run == -INFINITY ? 0.0f : l * __builtin_amdgcn_exp2f(m_run - M);
@@ -660,10 +673,7 @@ prefill_mx_kernel(FwdArgs a, int ntq, const int8_t* __restrict__ qc, const float
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = 32 * db + 8 * a4 + 4 * half;
       float o1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (PASS == 2) {
-        const f32x4 p = *(const f32x4*)(prow + d);
-        o1[0] = p[0]; o1[1] = p[1]; o1[2] = p[2]; o1[3] = p[3];
-      }
+      if constexpr (PASS == 2) get4<TO>(prow + d, o1);
       TO o4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) o4[r] = Elem<TO>::from_float(fmaf(w2, oacc[db][4 * a4 + r] * inv, w1 * o1[r]));

@@ -292,9 +292,9 @@ def test_mx_entry_points_reject_before_enqueue(lib):
     assert q4(FAKE, FAKE, FAKE, 1, 2, 64, 128, 2, 2, None) == E_INVALID
     assert q4(FAKE, FAKE + 4, FAKE, 1, 2, 64, 128, 1, 2, None) == E_INVALID   # misaligned codes
     # the diagonal-tiled mode also holds V's MXFP4 codes (half a byte per element)
-    # and scale bytes, and the fp32 row partials (D + 4 floats per query row)
+    # and scale bytes, and the row partials (D 16-bit values and 4 floats per query row)
     need3 = ws(1, 40, 40, 32760, 32760, 128, 0, 0, 0, 3, 2)
-    assert need3 >= need + 40 * 32760 * 128 // 2 + 40 * 32760 * 128 // 32 + 40 * 32760 * 132 * 4
+    assert need3 >= need + 40 * 32760 * 128 // 2 + 40 * 32760 * 128 // 32 + 40 * 32760 * (256 + 16)
 
 
 

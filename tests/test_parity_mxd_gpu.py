@@ -6,9 +6,10 @@ The FP4 quantiser (attn_quantize_mx4) must match the oracle's codes and scale
 bytes bit for bit, midpoints and saturation included (this also pins the
 rounding of the conversion instruction the kernel uses for its weights). The
 attention is compared with the oracle's emulation of the mode, which rounds
-every weight as the mode defines: what remains is fp32 arithmetic and the
-bf16/f16 rounding of the output (2^-9 relative), so MXD_REL = 1e-2 leaves a
-margin of five, for the whole output and for every single row (a weight whose
+every weight as the mode defines: what remains is fp32 arithmetic and two
+bf16/f16 roundings (2^-9 relative each: the first pass's partial rows and the
+output), so MXD_REL = 1e-2 leaves a margin of about four, for the whole output
+and for every single row (a weight whose
 exact value sat within an fp32 rounding of an E2M1 midpoint could round the
 other way and move its row by up to a third of that weight; the kernel forms
 each exponent exactly up to one fp32 rounding so that this stays out of
