@@ -122,7 +122,10 @@ typedef enum {
  *                partials. Given less than attn_fwd_workspace_bytes
  *                but at least what the unsplit schedule needs (0 for
  *                bf16/f16 inputs), the call runs unsplit: the same result
- *                up to rounding.
+ *                up to rounding. The low-precision modes hold their codes
+ *                and scales there; ATTN_MODE_MXD also V's MXFP4 codes and
+ *                one partial row per query row (D 16-bit values and 4
+ *                floats) that its second launch merges.
  *   stream       hipStream_t to enqueue on.
  *
  * A row with no visible key (window_lo > pos0 + i) is written as exact zeros.
