@@ -2,7 +2,8 @@
 through the C ABI: its results must equal attn_fwd's (same kernels, same
 plan; only the workspace differs) bit for bit, call after call on the same
 fixed device array, including a second, smaller call, inside a captured graph,
-and within the parity bar against the fp64 oracle."""
+and within the parity bar against the fp64 oracle (for the diagonal-tiled MX
+mode, against the oracle's emulation of that mode)."""
 import pytest
 import torch
 
@@ -65,6 +66,23 @@ def test_noalloc_fp32_staging_then_bf16_prefill():
         q, k, v, a, b = _pair(w)
         assert torch.equal(a, b)
         _oracle(a, q, k, v, w)
+
+
+def test_noalloc_diagonal_tiled_mx_two_calls_second_smaller():
+    # the diagonal-tiled mode keeps its codes, scales and row partials in the
+    # array; two launches per call, the second merging the first's partials
+    for w in (Workload("mxd_big", 1, 4, 2, 300, 700, 128, torch.bfloat16, causal=True, pos0=400,
+                       mode=sdpa.MODE_MXD),
+              Workload("mxd_small", 1, 2, 1, 97, 200, 64, torch.float16, pos0=37,
+                       mode=sdpa.MODE_MXD)):
+        announce(f"noalloc {w.name}")
+        q, k, v, a, b = _pair(w)
+        assert torch.equal(a, b)
+        ref = oracle.attn_mxd(q.cpu(), k.cpu(), v.cpu(), scale=w.scale, causal=w.causal,
+                              pos0=w.pos0)
+        rel, _ = metrics(a.double().cpu().numpy(), ref)
+        print(f"    rel(vs emulation)={rel:.3e}", flush=True)
+        assert rel <= 1e-2, rel
 
 
 def test_noalloc_too_large_is_refused():
