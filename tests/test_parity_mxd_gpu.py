@@ -199,3 +199,9 @@ def test_mxd_mode_with_rope():
     print(f"    rel(vs emulation on rotated inputs)={rel:.3e} rel(vs exact)={rel_ex:.3e}", flush=True)
     assert rel <= 2 * MXD_REL, rel
     assert rel_ex <= MXD_EXACT, rel_ex
+
+
+def test_mxd_mode_sdxl_1024px_sampled():
+    # head dim 64 at scale: 2 x 10 x 4096 x 64 bf16, 64 sampled rows
+    w = WORKLOADS["sdxl_1024px_bf16"].variant(name="sdxl_mxd", mode=sdpa.MODE_MXD)
+    _check(w, rows=sample_rows(w, 64))
